@@ -1,0 +1,294 @@
+// C ABI of libplc: host-side validation and dispatch.  Every check runs on the
+// host before anything is enqueued and uses host-visible arguments only; the
+// library refuses rather than guesses (a missing E4M3 scale is an error, not
+// an implied 1.0: ReVolta README, "E4M3 KV"; a context longer than the block
+// table can hold is rejected: ReVolta README, "Performance" and "Support and
+// limits").
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "../../include/plc.h"
+#include "plc_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+constexpr int kHeadDim = 128;
+constexpr int kBlockSize = 16;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_cache(const plc_kv_cache* kv) {
+    if (!kv) return fail(PLC_ERR_INVALID_ARG, "kv cache descriptor is NULL");
+    if (kv->dtype != PLC_KV_FP16 && kv->dtype != PLC_KV_E4M3 && kv->dtype != PLC_KV_INT8)
+        return fail(PLC_ERR_UNSUPPORTED, "kv dtype %d is not one of FP16(0), E4M3(1), INT8(2)",
+                    kv->dtype);
+    if (kv->head_dim != kHeadDim)
+        return fail(PLC_ERR_UNSUPPORTED, "head_dim %d: kernels are built for %d", kv->head_dim,
+                    kHeadDim);
+    if (kv->block_size != kBlockSize)
+        return fail(PLC_ERR_UNSUPPORTED, "block_size %d: kernels are built for %d", kv->block_size,
+                    kBlockSize);
+    if (kv->num_blocks <= 0 || kv->num_kv_heads <= 0)
+        return fail(PLC_ERR_INVALID_ARG, "num_blocks %d / num_kv_heads %d must be positive",
+                    kv->num_blocks, kv->num_kv_heads);
+    if (!kv->k_cache || !kv->v_cache) return fail(PLC_ERR_INVALID_ARG, "k_cache / v_cache is NULL");
+    if (kv->dtype != PLC_KV_FP16 && (!kv->k_scale || !kv->v_scale))
+        return fail(PLC_ERR_INVALID_ARG,
+                    "%s cache without %s scales: scales are required, never assumed 1.0",
+                    kv->dtype == PLC_KV_E4M3 ? "E4M3" : "INT8",
+                    kv->dtype == PLC_KV_E4M3 ? "per-head" : "per-token");
+    return PLC_OK;
+}
+
+int check_heads(int32_t num_q_heads, const plc_kv_cache* kv) {
+    if (num_q_heads <= 0 || num_q_heads % kv->num_kv_heads != 0)
+        return fail(PLC_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                    num_q_heads, kv->num_kv_heads);
+    const int G = num_q_heads / kv->num_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+        return fail(PLC_ERR_UNSUPPORTED, "GQA group size %d: supported are 1, 2, 4, 8, 16", G);
+    return PLC_OK;
+}
+
+int check_lengths(int32_t num_seqs, int32_t max_blocks, int32_t max_context_len, int32_t block_size) {
+    if (num_seqs <= 0) return fail(PLC_ERR_INVALID_ARG, "num_seqs %d must be positive", num_seqs);
+    if (max_blocks <= 0) return fail(PLC_ERR_INVALID_ARG, "max_blocks %d must be positive", max_blocks);
+    if (max_context_len < 0)
+        return fail(PLC_ERR_INVALID_ARG, "max_context_len %d is negative", max_context_len);
+    if ((int64_t)max_context_len > (int64_t)max_blocks * block_size)
+        return fail(PLC_ERR_INVALID_ARG,
+                    "max_context_len %d exceeds the block table's capacity %lld (%d blocks of %d)",
+                    max_context_len, (long long)max_blocks * block_size, max_blocks, block_size);
+    return PLC_OK;
+}
+
+plc::KvView view(const plc_kv_cache* kv) {
+    plc::KvView v;
+    v.k = kv->k_cache;
+    v.v = kv->v_cache;
+    v.k_scale = kv->k_scale;
+    v.v_scale = kv->v_scale;
+    v.num_blocks = kv->num_blocks;
+    v.num_kv_heads = kv->num_kv_heads;
+    v.dtype = kv->dtype;
+    return v;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(PLC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return PLC_OK;
+}
+
+int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                          int32_t partition_tokens) {
+    if (partition_tokens > 0) return partition_tokens;
+    // Enough partitions to give the 256 compute units several workgroups each,
+    // never shorter than 512 keys (merge traffic) nor longer than 4,096.
+    int64_t groups = (int64_t)num_seqs * num_kv_heads;
+    int32_t p = 4096;
+    while (p > 512 && groups * ((max_context_len + p - 1) / p) < 1024) p /= 2;
+    return p;
+}
+
+int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
+                 const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                 int32_t num_seqs, int32_t max_context_len, int32_t partition_tokens, float sm_scale,
+                 void* workspace, size_t workspace_bytes, plc::DecodeParams* out) {
+    int rc;
+    if ((rc = check_cache(kv))) return rc;
+    if ((rc = check_heads(num_q_heads, kv))) return rc;
+    if ((rc = check_lengths(num_seqs, max_blocks, max_context_len, kv->block_size))) return rc;
+    if (!q || !block_tables || !context_lens)
+        return fail(PLC_ERR_INVALID_ARG, "q / block_tables / context_lens is NULL");
+    if (partition_tokens < 0 || partition_tokens % kv->block_size != 0)
+        return fail(PLC_ERR_INVALID_ARG, "partition_tokens %d must be 0 or a multiple of block_size %d",
+                    partition_tokens, kv->block_size);
+    if (!std::isfinite(sm_scale)) return fail(PLC_ERR_INVALID_ARG, "sm_scale is not finite");
+    const int32_t P = resolve_partition(num_seqs, kv->num_kv_heads, max_context_len, partition_tokens);
+    const size_t need = plc_decode_workspace_size(num_seqs, num_q_heads, kv->head_dim,
+                                                  max_context_len, P);
+    if (!workspace || workspace_bytes < need)
+        return fail(PLC_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                    workspace_bytes, workspace, need);
+    const int32_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
+    const size_t rows = (size_t)num_seqs * num_q_heads;
+    plc::DecodeParams& p = *out;
+    p.q = q;
+    p.kv = view(kv);
+    p.block_tables = block_tables;
+    p.max_blocks = max_blocks;
+    p.context_lens = context_lens;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.max_context_len = max_context_len;
+    p.partition_tokens = P;
+    p.nparts = nparts;
+    p.qk_scale_log2 = sm_scale * 1.4426950408889634f;
+    p.o_parts = static_cast<float*>(workspace);
+    p.lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           align_up(rows * nparts * kv->head_dim * sizeof(float)));
+    return PLC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t plc_abi_version(void) { return PLC_ABI_VERSION; }
+
+const char* plc_last_error(void) { return g_err; }
+
+int plc_kv_append_quant(const plc_kv_cache* kv, const void* k_new, const void* v_new,
+                        const int32_t* block_tables, int32_t max_blocks,
+                        const int32_t* cu_new_lens, const int32_t* start_pos, int32_t num_seqs,
+                        int32_t total_new_tokens, void* stream) {
+    int rc;
+    if ((rc = check_cache(kv))) return rc;
+    if (num_seqs <= 0) return fail(PLC_ERR_INVALID_ARG, "num_seqs %d must be positive", num_seqs);
+    if (max_blocks <= 0) return fail(PLC_ERR_INVALID_ARG, "max_blocks %d must be positive", max_blocks);
+    if (total_new_tokens < 0)
+        return fail(PLC_ERR_INVALID_ARG, "total_new_tokens %d is negative", total_new_tokens);
+    if (total_new_tokens == 0) return PLC_OK;
+    if (!k_new || !v_new || !block_tables || !cu_new_lens || !start_pos)
+        return fail(PLC_ERR_INVALID_ARG, "k_new / v_new / block_tables / cu_new_lens / start_pos is NULL");
+    if ((int64_t)total_new_tokens * kv->num_kv_heads * 2 * 16 > ((int64_t)1 << 40))
+        return fail(PLC_ERR_INVALID_ARG, "total_new_tokens %d too large", total_new_tokens);
+    plc::AppendParams p;
+    p.kv = view(kv);
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.block_tables = block_tables;
+    p.max_blocks = max_blocks;
+    p.cu_new_lens = cu_new_lens;
+    p.start_pos = start_pos;
+    p.num_seqs = num_seqs;
+    p.total_new_tokens = total_new_tokens;
+    return hip_status(plc::launch_kv_append(p, static_cast<hipStream_t>(stream)), "kv_append_quant launch");
+}
+
+int plc_attn_prefill_paged(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
+                           const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* cu_q_lens, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                           int32_t max_context_len, float sm_scale, float* out, float* lse,
+                           void* stream) {
+    int rc;
+    if ((rc = check_cache(kv))) return rc;
+    if ((rc = check_heads(num_q_heads, kv))) return rc;
+    if ((rc = check_lengths(num_seqs, max_blocks, max_context_len, kv->block_size))) return rc;
+    if (total_q_tokens < 0 || max_q_len < 0)
+        return fail(PLC_ERR_INVALID_ARG, "total_q_tokens %d / max_q_len %d is negative",
+                    total_q_tokens, max_q_len);
+    if (max_q_len > max_context_len)
+        return fail(PLC_ERR_INVALID_ARG, "max_q_len %d exceeds max_context_len %d", max_q_len,
+                    max_context_len);
+    if (total_q_tokens == 0 || max_q_len == 0) return PLC_OK;
+    if (!q || !block_tables || !cu_q_lens || !context_lens || !out || !lse)
+        return fail(PLC_ERR_INVALID_ARG, "q / block_tables / cu_q_lens / context_lens / out / lse is NULL");
+    if (!std::isfinite(sm_scale)) return fail(PLC_ERR_INVALID_ARG, "sm_scale is not finite");
+    plc::PrefillParams p;
+    p.q = q;
+    p.kv = view(kv);
+    p.block_tables = block_tables;
+    p.max_blocks = max_blocks;
+    p.cu_q_lens = cu_q_lens;
+    p.context_lens = context_lens;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.max_q_len = max_q_len;
+    p.max_context_len = max_context_len;
+    p.qk_scale_log2 = sm_scale * 1.4426950408889634f;
+    p.out = out;
+    p.lse = lse;
+    return hip_status(plc::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+int32_t plc_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                    int32_t partition_tokens) {
+    return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+}
+
+size_t plc_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+    // the default partition shrinks as (sequence, KV head) groups get fewer;
+    // sizing with one KV head gives the shortest partition, so the bound holds
+    // for every head count
+    const int32_t P = partition_tokens > 0
+                          ? partition_tokens
+                          : resolve_partition(num_seqs, 1, max_context_len, 0);
+    const int64_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
+    const size_t rows = (size_t)num_seqs * num_q_heads;
+    return align_up(rows * nparts * head_dim * sizeof(float)) + align_up(rows * nparts * sizeof(float));
+}
+
+int plc_attn_decode_partials(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
+                             const int32_t* block_tables, int32_t max_blocks,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t max_context_len, int32_t partition_tokens, float sm_scale,
+                             void* workspace, size_t workspace_bytes, int32_t* nparts,
+                             size_t* lse_parts_offset, void* stream) {
+    plc::DecodeParams p;
+    int rc = decode_setup(q, num_q_heads, kv, block_tables, max_blocks, context_lens, num_seqs,
+                          max_context_len, partition_tokens, sm_scale, workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    if (nparts) *nparts = p.nparts;
+    if (lse_parts_offset)
+        *lse_parts_offset = (size_t)(reinterpret_cast<char*>(p.lse_parts) - static_cast<char*>(workspace));
+    return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)),
+                      "decode partition launch");
+}
+
+int plc_attn_decode_paged(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
+                          const int32_t* block_tables, int32_t max_blocks,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                          int32_t partition_tokens, float sm_scale, float* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    plc::DecodeParams p;
+    int rc = decode_setup(q, num_q_heads, kv, block_tables, max_blocks, context_lens, num_seqs,
+                          max_context_len, partition_tokens, sm_scale, workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    if (!out || !lse) return fail(PLC_ERR_INVALID_ARG, "out / lse is NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = hip_status(plc::launch_decode_partials(p, s), "decode partition launch"))) return rc;
+    return hip_status(plc::launch_lse_merge(p.o_parts, p.lse_parts, num_seqs * num_q_heads, p.nparts,
+                                            kv->head_dim, out, lse, s),
+                      "lse merge launch");
+}
+
+int plc_lse_merge(const float* o_parts, const float* lse_parts, int32_t rows, int32_t nparts,
+                  int32_t head_dim, float* out, float* lse_out, void* stream) {
+    if (rows < 0 || nparts < 1 || head_dim < 1 || head_dim > 512)
+        return fail(PLC_ERR_INVALID_ARG, "rows %d / nparts %d / head_dim %d out of range", rows,
+                    nparts, head_dim);
+    if (rows == 0) return PLC_OK;
+    if (!o_parts || !lse_parts || !out || !lse_out)
+        return fail(PLC_ERR_INVALID_ARG, "o_parts / lse_parts / out / lse_out is NULL");
+    return hip_status(plc::launch_lse_merge(o_parts, lse_parts, rows, nparts, head_dim, out, lse_out,
+                                            static_cast<hipStream_t>(stream)),
+                      "lse merge launch");
+}
+
+int plc_debug_e4m3_to_f16(const uint8_t* codes, uint16_t* out, int32_t n, void* stream) {
+    if (n < 0) return fail(PLC_ERR_INVALID_ARG, "n %d is negative", n);
+    if (n == 0) return PLC_OK;
+    if (!codes || !out) return fail(PLC_ERR_INVALID_ARG, "codes / out is NULL");
+    return hip_status(plc::launch_debug_e4m3(codes, out, n, static_cast<hipStream_t>(stream)),
+                      "debug e4m3 launch");
+}
+
+}  // extern "C"

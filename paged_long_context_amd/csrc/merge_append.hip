@@ -1,0 +1,183 @@
+// LSE merge of partial attention states, KV append with quantization, and the
+// E4M3 conversion diagnostic, for gfx950.
+#include "plc_device.h"
+#include "plc_internal.h"
+
+namespace plc {
+namespace {
+
+// ------------------------------------------------------------------ merge
+//
+// One wave per row.  Parts are visited in index order (1Cat-vLLM README,
+// Layer 2 "Split-KV3": the fp32 partial states of the partitions are combined),
+// so the result does not depend on how the rows are scheduled.
+constexpr int kMergeRowsPerBlock = 4;
+
+template <int VPL>   // values per lane: head_dim <= 64 * VPL
+__global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(
+    const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int rows, int nparts,
+    int D, float* __restrict__ out, float* __restrict__ lse_out) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float* lp = lse_parts + (int64_t)row * nparts;
+    float M = -__builtin_inff();
+    for (int k = lane; k < nparts; k += 64) M = fmaxf(M, lp[k]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+    float acc[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) acc[v] = 0.0f;
+    float wsum = 0.0f;
+    if (M != -__builtin_inff()) {
+        const float* op = o_parts + (int64_t)row * nparts * D;
+        for (int k = 0; k < nparts; ++k) {
+            const float lk = lp[k];
+            const float w = (lk == -__builtin_inff()) ? 0.0f : fast_exp2((lk - M) * kLog2e);
+            wsum += w;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int d = lane + 64 * v;
+                if (d < D) acc[v] += w * op[(int64_t)k * D + d];
+            }
+        }
+    }
+    const bool empty = !(wsum > 0.0f);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int d = lane + 64 * v;
+        if (d < D) out[(int64_t)row * D + d] = empty ? 0.0f : acc[v] / wsum;
+    }
+    if (lane == 0) lse_out[row] = empty ? -__builtin_inff() : M + __builtin_logf(wsum);
+}
+
+// ------------------------------------------------------------------ append
+//
+// Sixteen lanes per (token, KV head, K-or-V) row of 128 fp16 values, eight
+// values per lane (one 16-byte load).  E4M3 divides by the head's scale in
+// IEEE fp32 and rounds to nearest-even; INT8 takes the row's absolute maximum
+// across the sixteen lanes first (ReVolta README, "INT8 KV": scales per token
+// and head at run time).
+constexpr int kAppendThreads = 256;
+
+template <int KV>
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams p) {
+    constexpr int D = 128, BS = 16;
+    const int64_t gid = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
+    const int Hkv = p.kv.num_kv_heads;
+    const int64_t row = gid >> 4;                 // (token, head, kv) row
+    const int part = (int)(gid & 15);             // 8-value slice of the row
+    const int64_t nrows = (int64_t)p.total_new_tokens * Hkv * 2;
+    const bool live = row < nrows;
+    const int64_t r = live ? row : 0;
+    const int which = (int)(r & 1);               // 0: K, 1: V
+    const int h = (int)((r >> 1) % Hkv);
+    const int t = (int)((r >> 1) / Hkv);
+
+    // sequence of token t: last b with cu_new_lens[b] <= t
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.cu_new_lens[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int pos = p.start_pos[b] + (t - p.cu_new_lens[b]);
+    const int lb = pos / BS;
+    int blk = (lb >= 0 && lb < p.max_blocks) ? p.block_tables[(int64_t)b * p.max_blocks + lb] : -1;
+    const bool ok = live && blk >= 0 && blk < p.kv.num_blocks && pos >= 0;
+    const int slot = pos - lb * BS;
+
+    const f16* src = static_cast<const f16*>(which ? p.v_new : p.k_new) +
+                     ((int64_t)t * Hkv + h) * D + 8 * part;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
+    const f16x8 x = __builtin_bit_cast(f16x8, raw);
+    const int64_t crow = ((int64_t)(ok ? blk : 0) * Hkv + h) * BS + slot;
+
+    if constexpr (KV == KV_FP16) {
+        if (ok) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(const_cast<void*>(
+                    which ? p.kv.v : p.kv.k)) + crow * D + 8 * part) = raw;
+    } else if constexpr (KV == KV_E4M3) {
+        const float s = (which ? p.kv.v_scale : p.kv.k_scale)[h];
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t c = f32_to_e4m3((float)x[e] / s);
+            w[e >> 2] |= c << (8 * (e & 3));
+        }
+        if (ok) *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(const_cast<void*>(
+                    which ? p.kv.v : p.kv.k)) + crow * D + 8 * part) = u32x2{w[0], w[1]};
+    } else {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf((float)x[e]));
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor(m, off));
+        const float sigma = m / 127.0f;
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float q = 0.0f;
+            if (sigma != 0.0f) {
+                q = __builtin_rintf((float)x[e] / sigma);
+                q = fminf(fmaxf(q, -127.0f), 127.0f);
+            }
+            w[e >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (e & 3));
+        }
+        if (ok) {
+            *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(const_cast<void*>(
+                which ? p.kv.v : p.kv.k)) + crow * D + 8 * part) = u32x2{w[0], w[1]};
+            if (part == 0) const_cast<float*>(which ? p.kv.v_scale : p.kv.k_scale)[crow] = sigma;
+        }
+    }
+}
+
+__global__ void debug_e4m3_kernel(const uint8_t* codes, uint16_t* out, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const f16x2 v = e4m3x2_to_f16x2<false>((uint32_t)codes[i]);
+    out[i] = __builtin_bit_cast(uint16_t, v[0]);
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_t rows,
+                            int32_t nparts, int32_t head_dim, float* out, float* lse_out,
+                            hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    dim3 grid((rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock);
+    dim3 block(64 * kMergeRowsPerBlock);
+    if (head_dim <= 64)
+        hipLaunchKernelGGL(lse_merge_kernel<1>, grid, block, 0, s, o_parts, lse_parts, rows, nparts,
+                           head_dim, out, lse_out);
+    else if (head_dim <= 128)
+        hipLaunchKernelGGL(lse_merge_kernel<2>, grid, block, 0, s, o_parts, lse_parts, rows, nparts,
+                           head_dim, out, lse_out);
+    else if (head_dim <= 256)
+        hipLaunchKernelGGL(lse_merge_kernel<4>, grid, block, 0, s, o_parts, lse_parts, rows, nparts,
+                           head_dim, out, lse_out);
+    else
+        hipLaunchKernelGGL(lse_merge_kernel<8>, grid, block, 0, s, o_parts, lse_parts, rows, nparts,
+                           head_dim, out, lse_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {
+    const int64_t threads = (int64_t)p.total_new_tokens * p.kv.num_kv_heads * 2 * 16;
+    if (threads == 0) return hipSuccess;
+    dim3 grid((unsigned)((threads + kAppendThreads - 1) / kAppendThreads));
+    switch (p.kv.dtype) {
+    case KV_FP16: hipLaunchKernelGGL(kv_append_kernel<KV_FP16>, grid, dim3(kAppendThreads), 0, s, p); break;
+    case KV_E4M3: hipLaunchKernelGGL(kv_append_kernel<KV_E4M3>, grid, dim3(kAppendThreads), 0, s, p); break;
+    case KV_INT8: hipLaunchKernelGGL(kv_append_kernel<KV_INT8>, grid, dim3(kAppendThreads), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_e4m3(const uint8_t* codes, uint16_t* out, int32_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(debug_e4m3_kernel, dim3((n + 255) / 256), dim3(256), 0, s, codes, out, n);
+    return hipGetLastError();
+}
+
+}  // namespace plc

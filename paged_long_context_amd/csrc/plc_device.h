@@ -1,0 +1,140 @@
+// Device helpers shared by the gfx950 kernels of libplc.
+//
+// Vector types, the KV codecs (E4M3 <-> fp16, INT8 -> fp16), MFMA wrappers and
+// wave-level shuffles.  Everything here is CDNA4 (gfx950) specific.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace plc {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum KvType { KV_FP16 = 0, KV_E4M3 = 1, KV_INT8 = 2 };
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------------ codecs
+
+// Two E4M3FN codes (bytes 2*hi and 2*hi+1 of w) -> two fp16 values.  Exact:
+// every finite E4M3FN value is an fp16 value; the hardware converter on
+// gfx950 reads OCP E4M3FN.
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+// Four E4M3 codes in a dword -> f16x4 (byte order kept).
+__device__ __forceinline__ f16x4 e4m3x4_to_f16x4(uint32_t w) {
+    f16x2 a = e4m3x2_to_f16x2<false>(w);
+    f16x2 b = e4m3x2_to_f16x2<true>(w);
+    return f16x4{a[0], a[1], b[0], b[1]};
+}
+
+// Eight codes in two dwords -> one MFMA operand.
+__device__ __forceinline__ f16x8 e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
+    f16x2 a = e4m3x2_to_f16x2<false>(lo);
+    f16x2 b = e4m3x2_to_f16x2<true>(lo);
+    f16x2 c = e4m3x2_to_f16x2<false>(hi);
+    f16x2 d = e4m3x2_to_f16x2<true>(hi);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Two signed int8 codes (bytes 2*hi, 2*hi+1 of w) -> fp16, exact: the byte
+// plus 128 becomes the low mantissa byte of 1024 + u, then 1152 is removed.
+template <bool HI>
+__device__ __forceinline__ f16x2 i8x2_to_f16x2(uint32_t w) {
+    uint32_t u = w ^ 0x80808080u;
+    constexpr uint32_t sel = HI ? 0x04030402u : 0x04010400u;
+    uint32_t bits = __builtin_amdgcn_perm(0x64646464u, u, sel);
+    f16x2 x = __builtin_bit_cast(f16x2, bits);
+    return x - f16x2{(f16)1152.0f, (f16)1152.0f};
+}
+
+__device__ __forceinline__ f16x8 i8x8_to_f16x8(uint32_t lo, uint32_t hi) {
+    f16x2 a = i8x2_to_f16x2<false>(lo);
+    f16x2 b = i8x2_to_f16x2<true>(lo);
+    f16x2 c = i8x2_to_f16x2<false>(hi);
+    f16x2 d = i8x2_to_f16x2<true>(hi);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int KV, bool HI>
+__device__ __forceinline__ f16x2 codes2_to_f16x2(uint32_t w) {
+    if constexpr (KV == KV_E4M3)
+        return e4m3x2_to_f16x2<HI>(w);
+    else
+        return i8x2_to_f16x2<HI>(w);
+}
+
+template <int KV>
+__device__ __forceinline__ f16x8 codes8_to_f16x8(uint32_t lo, uint32_t hi) {
+    if constexpr (KV == KV_E4M3)
+        return e4m3x8_to_f16x8(lo, hi);
+    else
+        return i8x8_to_f16x8(lo, hi);
+}
+
+// fp32 -> nearest E4M3FN code, ties to even, saturating at 448, NaN kept.
+// Integer rounding on the fp32 bit pattern: normals drop 20 mantissa bits with
+// round-half-even; magnitudes below 2^-6 are multiples of 2^-9 after rounding.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a > 0x7F800000u) {
+        code = 0x7Fu;                                  // NaN
+    } else if (a >= 0x43E00000u) {                     // >= 448 (and inf)
+        code = 0x7Eu;
+    } else if (a < 0x3C800000u) {                      // < 2^-6: subnormal grid
+        float af = __builtin_bit_cast(float, a);
+        code = (uint32_t)__builtin_rintf(af * 512.0f); // 0..8; 8 is 2^-6
+    } else {
+        uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+        code = r - (120u << 3);                        // rebias exponent 127 -> 7
+    }
+    return code | sign;
+}
+
+// ------------------------------------------------------------------ MFMA
+
+// D(16x16) += A(16x32) * B(32x16), f16 inputs, fp32 accumulate.
+// Lane l holds A row l%16, B column l%16 (8 K-values each, slot group l/16)
+// and D rows 4*(l/16)+0..3 of column l%16.
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32) += A(32x16) * B(16x32).  Lane l holds A row l%32, B column l%32
+// (8 K-values, slot group l/32) and D[8*(r/4) + 4*(l/32) + r%4][l%32], r < 16.
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ shuffles
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) {
+    int lane = __lane_id();
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2,
+                                                                  __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T>
+__device__ __forceinline__ T load_nt(const T* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+}  // namespace plc

@@ -1,0 +1,77 @@
+// Host-side launch interfaces between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace plc {
+
+struct KvView {
+    const void* k;          // [num_blocks][Hkv][block_size][D] elements
+    const void* v;
+    const float* k_scale;   // E4M3: [Hkv]; INT8: [num_blocks][Hkv][block_size]
+    const float* v_scale;
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t dtype;
+};
+
+// Decode: per-partition normalized partial outputs and natural-log LSEs.
+struct DecodeParams {
+    const void* q;              // f16 [B][Hq][D]
+    KvView kv;
+    const int32_t* block_tables;
+    int32_t max_blocks;
+    const int32_t* context_lens;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t max_context_len;    // device lengths are clamped to it
+    int32_t partition_tokens;   // multiple of 16
+    int32_t nparts;
+    float qk_scale_log2;        // sm_scale * log2(e)
+    float* o_parts;             // [B*Hq][nparts][D]
+    float* lse_parts;           // [B*Hq][nparts]
+};
+
+hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s);
+
+hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_t rows,
+                            int32_t nparts, int32_t head_dim, float* out, float* lse_out,
+                            hipStream_t s);
+
+struct AppendParams {
+    KvView kv;                  // k/v/scales written through const_cast by the kernel
+    const void* k_new;          // f16 [T][Hkv][D]
+    const void* v_new;
+    const int32_t* block_tables;
+    int32_t max_blocks;
+    const int32_t* cu_new_lens;
+    const int32_t* start_pos;
+    int32_t num_seqs;
+    int32_t total_new_tokens;
+};
+
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
+
+struct PrefillParams {
+    const void* q;              // f16 [T][Hq][D]
+    KvView kv;
+    const int32_t* block_tables;
+    int32_t max_blocks;
+    const int32_t* cu_q_lens;
+    const int32_t* context_lens;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t max_q_len;
+    int32_t max_context_len;    // device lengths are clamped to it
+    float qk_scale_log2;
+    float* out;                 // f32 [T][Hq][D]
+    float* lse;                 // f32 [T][Hq]
+};
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+
+hipError_t launch_debug_e4m3(const uint8_t* codes, uint16_t* out, int32_t n, hipStream_t s);
+
+}  // namespace plc

@@ -1,0 +1,349 @@
+// Chunked causal prefill over the paged KV cache, for gfx950.
+//
+// Workgroup = 4 waves = 256 query rows of one KV head; a row is a (query
+// position, query head) pair, positions outer, so the G query heads that read
+// one KV head share every K/V tile (1Cat-vLLM README, Layer 2 "GQA Multi-Head
+// Packing").  Each wave owns 64 rows as two 32-row MFMA tiles and keeps their
+// Q operands and O accumulators in registers for the whole key loop.
+//
+// Keys are walked in tiles of 64 (four 16-token pages).  Per tile the
+// workgroup gathers the pages' codes with 16- and 8-byte loads (one page id per
+// page), converts them to fp16 exactly and writes K as [key][d] and V already
+// transposed as [d][key] into one of two LDS buffers; the next tile's loads are
+// in flight while the current tile is computed (Layer 1 and the
+// "Software-Reconstructed Async" section describe the same goals with V100
+// means).  Each wave then forms S^T = K Q^T on 32x32x16 f16 MFMA with fp32
+// accumulation, runs the online softmax per query row in fp32 (Layer 2 "N32
+// Online Softmax"; "Performance First": fp32 QK/PV), and accumulates
+// O^T = V^T P^T on MFMA ("Wide QK / PV").  Tiles wholly below the chunk's first
+// position skip the causal mask; only the tiles at the diagonal apply it
+// (Layer 2 "Prefix / Causal-Tail Separation").
+#include "plc_device.h"
+#include "plc_internal.h"
+
+namespace plc {
+namespace {
+
+constexpr int D = 128;
+constexpr int BS = 16;
+constexpr int KT = 64;                  // keys per tile
+constexpr int NWAVE = 4;
+constexpr int ROWS = 64 * NWAVE;        // query rows per workgroup
+constexpr int KSTR = D + 8;             // K row stride in LDS (halves)
+constexpr int VSTR = KT + 8;            // V^T row stride in LDS (halves)
+constexpr int KBUF = KT * KSTR;         // halves
+constexpr int VBUF = D * VSTR;          // halves
+
+// Which key of a 32-key subtile MFMA row rho of S^T holds: the swap of bits 2
+// and 3 makes the eight keys a lane owns for one PV step consecutive.
+__device__ __forceinline__ int key_of_row(int rho) {
+    return (rho & 0x13) | ((rho & 0x8) >> 1) | ((rho & 0x4) << 1);
+}
+
+template <int KV>
+struct Stage {
+    // Per thread: K of key t>>2, d = 32*(t&3) + [0,32); V of keys 4*(t>>4) + [0,4),
+    // d = 8*(t&15) + [0,8).
+    u32x4 k[(KV == KV_FP16) ? 4 : 2];
+    u32x4 v16[(KV == KV_FP16) ? 4 : 1];
+    u32x2 v8[(KV == KV_FP16) ? 1 : 4];
+    float ks, vs[4];
+};
+
+template <int KV>
+__device__ __forceinline__ void stage_load(Stage<KV>& st, const PrefillParams& p, int kvh, int k0,
+                                           int kend, int pg_k, const int pg_v[1], int tid) {
+    constexpr int EB = (KV == KV_FP16) ? 2 : 1;
+    const int Hkv = p.kv.num_kv_heads;
+    const uint8_t* kc = static_cast<const uint8_t*>(p.kv.k);
+    const uint8_t* vc = static_cast<const uint8_t*>(p.kv.v);
+    {   // K
+        const int key = k0 + (tid >> 2);
+        const bool ok = key < kend && pg_k >= 0 && pg_k < p.kv.num_blocks;
+        const int64_t rowb = (((int64_t)(ok ? pg_k : 0) * Hkv + kvh) * BS + (key & (BS - 1))) * D * EB;
+        const uint8_t* src = kc + rowb + 32 * (tid & 3) * EB;
+#pragma unroll
+        for (int j = 0; j < ((KV == KV_FP16) ? 4 : 2); ++j)
+            st.k[j] = ok ? *reinterpret_cast<const u32x4*>(src + 16 * j) : u32x4{0, 0, 0, 0};
+        if constexpr (KV == KV_INT8)
+            st.ks = ok ? p.kv.k_scale[((int64_t)pg_k * Hkv + kvh) * BS + (key & (BS - 1))] : 0.0f;
+    }
+    {   // V: four consecutive keys share one page (4 | 16)
+        const int key0 = k0 + 4 * (tid >> 4);
+        const int pg = pg_v[0];
+        const bool pgok = pg >= 0 && pg < p.kv.num_blocks;
+        const int64_t pb = pgok ? pg : 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key = key0 + e;
+            const bool ok = pgok && key < kend;
+            const uint8_t* src =
+                vc + (((pb * Hkv + kvh) * BS + (key & (BS - 1))) * D + 8 * (tid & 15)) * EB;
+            if constexpr (KV == KV_FP16)
+                st.v16[e] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+            else
+                st.v8[e] = ok ? *reinterpret_cast<const u32x2*>(src) : u32x2{0, 0};
+            if constexpr (KV == KV_INT8)
+                st.vs[e] = ok ? p.kv.v_scale[(pb * Hkv + kvh) * BS + (key & (BS - 1))] : 0.0f;
+        }
+    }
+}
+
+template <int KV>
+__device__ __forceinline__ void stage_store(const Stage<KV>& st, f16* lk, f16* lv, float* lks,
+                                            float* lvs, int tid) {
+    {   // K -> [key][d]
+        f16* dst = lk + (tid >> 2) * KSTR + 32 * (tid & 3);
+        if constexpr (KV == KV_FP16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(dst + 8 * j) = st.k[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                *reinterpret_cast<f16x8*>(dst + 16 * j) = codes8_to_f16x8<KV>(st.k[j][0], st.k[j][1]);
+                *reinterpret_cast<f16x8*>(dst + 16 * j + 8) = codes8_to_f16x8<KV>(st.k[j][2], st.k[j][3]);
+            }
+        }
+        if constexpr (KV == KV_INT8)
+            if ((tid & 3) == 0) lks[tid >> 2] = st.ks;
+    }
+    {   // V -> [d][key]: row 8*(t&15) + col, keys 4*(t>>4) + [0,4)
+        f16* dst = lv + (8 * (tid & 15)) * VSTR + 4 * (tid >> 4);
+        if constexpr (KV == KV_FP16) {
+#pragma unroll
+            for (int col = 0; col < 8; ++col) {
+                const uint32_t sel = (col & 1) ? 0x07060302u : 0x05040100u;
+                u32x2 r;
+                r[0] = __builtin_amdgcn_perm(st.v16[1][col >> 1], st.v16[0][col >> 1], sel);
+                r[1] = __builtin_amdgcn_perm(st.v16[3][col >> 1], st.v16[2][col >> 1], sel);
+                *reinterpret_cast<u32x2*>(dst + col * VSTR) = r;
+            }
+        } else {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f16x2 pr[2][4];
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const uint32_t a = st.v8[2 * pp + 1][hf], b = st.v8[2 * pp][hf];
+                    const uint32_t p01 = __builtin_amdgcn_perm(a, b, 0x05010400u);
+                    const uint32_t p23 = __builtin_amdgcn_perm(a, b, 0x07030602u);
+                    pr[pp][0] = codes2_to_f16x2<KV, false>(p01);
+                    pr[pp][1] = codes2_to_f16x2<KV, true>(p01);
+                    pr[pp][2] = codes2_to_f16x2<KV, false>(p23);
+                    pr[pp][3] = codes2_to_f16x2<KV, true>(p23);
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    *reinterpret_cast<f16x4*>(dst + (4 * hf + c) * VSTR) =
+                        f16x4{pr[0][c][0], pr[0][c][1], pr[1][c][0], pr[1][c][1]};
+            }
+        }
+        if constexpr (KV == KV_INT8)
+            if ((tid & 15) == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lvs[4 * (tid >> 4) + e] = st.vs[e];
+            }
+    }
+}
+
+template <int KV>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+    __shared__ __attribute__((aligned(16))) f16 s_k[2][KBUF];
+    __shared__ __attribute__((aligned(16))) f16 s_v[2][VBUF];
+    __shared__ float s_ks[2][KT], s_vs[2][KT];
+
+    const int tile = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int Hq = p.num_q_heads, G = Hq / p.kv.num_kv_heads;
+    const int qa = p.cu_q_lens[b];
+    // lengths beyond the host-stated bounds are clamped so that no page id
+    // outside the table is ever read
+    const int L = max(0, min(p.context_lens[b], p.max_context_len));
+    const int n = min(min(p.cu_q_lens[b + 1] - qa, p.max_q_len), L);
+    const int ppw = ROWS / G;                        // positions per workgroup
+    const int q0 = tile * ppw;
+    if (q0 >= n) return;
+    const int base = L - n;                          // position of the chunk's first token
+    const int qlast = min(q0 + ppw, n) - 1;
+    const int kend = base + qlast + 1;               // keys [0, kend) are visible to someone
+    const int kfull = base + q0 + 1;                 // keys [0, kfull) are visible to every row
+    const int ntiles = (kend + KT - 1) / KT;
+    const int nfull = kfull / KT;                    // tiles needing no mask
+    const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
+
+    // ---- Q operands: lane holds row l%32 of row-tile rt, d = 16kc + 8(l/32) + [0,8)
+    const int h32 = lane >> 5, r32 = lane & 31;
+    f16x8 qop[2][8];
+    int rowpos[2];
+    int64_t rowid[2];
+    bool rowok[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int r = 64 * wave + 32 * rt + r32;
+        const int po = q0 + r / G;
+        rowok[rt] = po < n;
+        const int poc = rowok[rt] ? po : qlast;
+        rowpos[rt] = base + poc;
+        rowid[rt] = (int64_t)(qa + poc) * Hq + kvh * G + (r % G);
+        const f16* q = static_cast<const f16*>(p.q) + rowid[rt] * D + 8 * h32;
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) qop[rt][kc] = *reinterpret_cast<const f16x8*>(q + 16 * kc);
+    }
+    float cscale = p.qk_scale_log2;
+    if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
+    float vscale = 1.0f;
+    if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
+    if constexpr (KV == KV_INT8) vscale = 1.0f / 256.0f;
+
+    float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
+    float l_run[2] = {0.0f, 0.0f};
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[rt][dt][r] = 0.0f;
+
+    // page ids: K staging thread reads key k0 + (t>>2), V staging keys k0 + 4(t>>4)
+    auto page_k = [&](int k0) {
+        const int key = k0 + (tid >> 2);
+        return key < kend ? bt[key / BS] : -1;
+    };
+    auto page_v = [&](int k0) {
+        const int key = k0 + 4 * (tid >> 4);
+        return key < kend ? bt[key / BS] : -1;
+    };
+
+    Stage<KV> st;
+    int pk_next = page_k(0), pv_next[1] = {page_v(0)};
+    stage_load<KV>(st, p, kvh, 0, kend, pk_next, pv_next, tid);
+    if (ntiles > 1) { pk_next = page_k(KT); pv_next[0] = page_v(KT); }
+    stage_store<KV>(st, s_k[0], s_v[0], s_ks[0], s_vs[0], tid);
+    __syncthreads();
+
+    const int krow = key_of_row(r32);
+    for (int j = 0; j < ntiles; ++j) {
+        const int k0 = j * KT;
+        const int buf = j & 1;
+        if (j + 1 < ntiles) {
+            stage_load<KV>(st, p, kvh, k0 + KT, kend, pk_next, pv_next, tid);
+            if (j + 2 < ntiles) { pk_next = page_k(k0 + 2 * KT); pv_next[0] = page_v(k0 + 2 * KT); }
+        }
+        const f16* lk = s_k[buf];
+        const f16* lv = s_v[buf];
+
+        // S^T[key][row] for two 32-key subtiles and both row-tiles
+        f32x16 s[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[ks][rt][r] = 0.0f;
+            const f16* krp = lk + (32 * ks + krow) * KSTR + 8 * h32;
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) {
+                const f16x8 a = *reinterpret_cast<const f16x8*>(krp + 16 * kc);
+                s[ks][0] = mfma32(a, qop[0][kc], s[ks][0]);
+                s[ks][1] = mfma32(a, qop[1][kc], s[ks][1]);
+            }
+        }
+        const bool masked = j >= nfull;
+        f16x8 pop[2][2][2];                          // [rt][ks][half]
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            float x[2][16];
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float v = s[ks][rt][r] * cscale;
+                    if constexpr (KV == KV_INT8)
+                        v *= s_ks[buf][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)];
+                    if (masked) {
+                        const int key = k0 + 32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7);
+                        v = (key <= rowpos[rt]) ? v : -__builtin_inff();
+                    }
+                    x[ks][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run[rt], mx);
+            const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+            const float alpha = fast_exp2(m_run[rt] - m_use);
+            float psum = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pe = fast_exp2(x[ks][r] - m_use);
+                    psum += pe;
+                    if constexpr (KV == KV_INT8)
+                        pe *= s_vs[buf][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)] * 256.0f;
+                    pop[rt][ks][r >> 3][r & 7] = (f16)pe;
+                }
+            l_run[rt] = l_run[rt] * alpha + psum;
+            m_run[rt] = m_new;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) acc[rt][dt] *= alpha;
+            }
+        }
+        // O^T[d][row] += V^T[d][key] P^T[key][row]
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const f16* vrp = lv + (32 * dt + r32) * VSTR + 8 * h32;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const f16x8 a = *reinterpret_cast<const f16x8*>(vrp + 32 * ks + 16 * hf);
+                    acc[0][dt] = mfma32(a, pop[0][ks][hf], acc[0][dt]);
+                    acc[1][dt] = mfma32(a, pop[1][ks][hf], acc[1][dt]);
+                }
+        }
+        if (j + 1 < ntiles)
+            stage_store<KV>(st, s_k[buf ^ 1], s_v[buf ^ 1], s_ks[buf ^ 1], s_vs[buf ^ 1], tid);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lanes l and l^32 hold halves of the same row's keys
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        float l = l_run[rt] + shfl_xor(l_run[rt], 32);
+        if (!rowok[rt]) continue;
+        const float inv = vscale / l;
+        float* o = p.out + rowid[rt] * D;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d = 32 * dt + 8 * a4 + 4 * h32;
+                f32x4 v = f32x4{acc[rt][dt][4 * a4 + 0], acc[rt][dt][4 * a4 + 1],
+                                acc[rt][dt][4 * a4 + 2], acc[rt][dt][4 * a4 + 3]} * inv;
+                *reinterpret_cast<f32x4*>(o + d) = v;
+            }
+        if (h32 == 0) p.lse[rowid[rt]] = (m_run[rt] + __builtin_log2f(l)) * kLn2;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
+    const int G = p.num_q_heads / p.kv.num_kv_heads;
+    const int ppw = ROWS / G;
+    dim3 grid((p.max_q_len + ppw - 1) / ppw, p.kv.num_kv_heads, p.num_seqs);
+    if (grid.x == 0) return hipSuccess;
+    switch (p.kv.dtype) {
+    case KV_FP16: hipLaunchKernelGGL(prefill_kernel<KV_FP16>, grid, dim3(256), 0, s, p); break;
+    case KV_E4M3: hipLaunchKernelGGL(prefill_kernel<KV_E4M3>, grid, dim3(256), 0, s, p); break;
+    case KV_INT8: hipLaunchKernelGGL(prefill_kernel<KV_INT8>, grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace plc

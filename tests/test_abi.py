@@ -1,0 +1,132 @@
+"""The C-ABI library loads, exports what include/plc.h declares, and refuses bad
+arguments on the host before touching the GPU (CPU only: no kernel runs)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "plc.h")
+
+
+@pytest.fixture(scope="module")
+def plc():
+    import paged_long_context_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(plc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["plc_kv_append_quant", "plc_attn_prefill_paged", "plc_attn_decode_paged",
+              "plc_lse_merge", "plc_attn_decode_partials", "plc_decode_workspace_size",
+              "plc_abi_version", "plc_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(plc):
+    lib = ctypes.CDLL(plc.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing
+
+
+def test_abi_version(plc):
+    assert plc.lib().plc_abi_version() == plc.ABI_VERSION == 1
+
+
+def _desc(plc, dtype=1, head_dim=128, block_size=16, num_blocks=10, hkv=1, scales=True):
+    fake = 0x1000  # never dereferenced: every call below fails validation first
+    return plc.plc_kv_cache(fake, fake, fake if scales else None, fake if scales else None,
+                            num_blocks, block_size, hkv, head_dim, dtype)
+
+
+def _decode(plc, desc, hq=8, max_blocks=4, max_ctx=64, part=0, ws_bytes=1 << 20, ws=0x2000,
+            q=0x3000):
+    return plc.lib().plc_attn_decode_paged(q, hq, ctypes.byref(desc), 0x4000, max_blocks, 0x5000, 2,
+                                           max_ctx, part, 0.088, 0x6000, 0x7000, ws, ws_bytes, None)
+
+
+def _err(plc):
+    return plc.lib().plc_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dtype=7), -2, "dtype"),
+    (dict(head_dim=64), -2, "head_dim"),
+    (dict(block_size=32), -2, "block_size"),
+    (dict(scales=False), -1, "never assumed 1.0"),
+    (dict(num_blocks=0), -1, "num_blocks"),
+])
+def test_cache_descriptor_is_validated(plc, kw, code, msg):
+    assert _decode(plc, _desc(plc, **kw)) == code
+    assert msg in _err(plc)
+
+
+def test_fp16_cache_needs_no_scales(plc):
+    # fails later, on the workspace, proving the scale check passed
+    assert _decode(plc, _desc(plc, dtype=0, scales=False), ws=None) == -3
+
+
+def test_int8_cache_needs_scales(plc):
+    assert _decode(plc, _desc(plc, dtype=2, scales=False)) == -1
+
+
+@pytest.mark.parametrize("hq,code", [(12, -1), (3, -2), (24, -2), (32, -2)])
+def test_group_size_is_validated(plc, hq, code):
+    assert _decode(plc, _desc(plc, hkv=1 if hq != 12 else 8), hq=hq) == code
+
+
+def test_context_longer_than_table_is_refused(plc):
+    assert _decode(plc, _desc(plc), max_blocks=4, max_ctx=65) == -1
+    assert "capacity" in _err(plc)
+
+
+def test_partition_must_be_block_multiple(plc):
+    assert _decode(plc, _desc(plc), part=24) == -1
+    assert "multiple" in _err(plc)
+
+
+def test_workspace_too_small(plc):
+    need = plc.decode_workspace_size(2, 8, 128, 64, 0)
+    assert need > 0
+    assert _decode(plc, _desc(plc), ws_bytes=need - 1) == -3
+    assert "needed" in _err(plc)
+
+
+def test_null_query_refused(plc):
+    assert _decode(plc, _desc(plc), q=None) == -1
+
+
+def test_workspace_size_formula(plc):
+    # rows * nparts * D floats + rows * nparts floats, each 256-byte aligned
+    rows, nparts = 8 * 8, 16
+    want = ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
+    assert plc.decode_workspace_size(8, 8, 128, 32768, 2048) == want
+
+
+def test_default_partition_choice(plc):
+    p = plc.decode_partition_tokens(8, 1, 32768, 0)
+    assert p % 16 == 0 and 512 <= p <= 4096
+    assert plc.decode_partition_tokens(8, 1, 32768, 2048) == 2048
+
+
+def test_prefill_and_merge_and_append_validation(plc):
+    L = plc.lib()
+    d = _desc(plc)
+    assert L.plc_attn_prefill_paged(0x1, 8, ctypes.byref(d), 0x1, 4, 0x1, 0x1, 1, 10, 100, 64,
+                                    0.1, 0x1, 0x1, None) == -1      # max_q_len > max_context_len
+    assert L.plc_attn_prefill_paged(None, 8, ctypes.byref(d), 0x1, 4, 0x1, 0x1, 1, 10, 10, 64,
+                                    0.1, 0x1, 0x1, None) == -1      # null q
+    assert L.plc_lse_merge(0x1, 0x1, 4, 0, 128, 0x1, 0x1, None) == -1
+    assert L.plc_lse_merge(0x1, 0x1, 4, 2, 1024, 0x1, 0x1, None) == -1
+    assert L.plc_lse_merge(None, 0x1, 4, 2, 128, 0x1, 0x1, None) == -1
+    assert L.plc_lse_merge(None, None, 0, 2, 128, None, None, None) == 0   # nothing to do
+    assert L.plc_kv_append_quant(ctypes.byref(d), None, 0x1, 0x1, 4, 0x1, 0x1, 1, 5, None) == -1
+    assert L.plc_kv_append_quant(ctypes.byref(d), None, None, None, 4, None, None, 1, 0, None) == 0
+    assert L.plc_kv_append_quant(ctypes.byref(d), 0x1, 0x1, 0x1, 4, 0x1, 0x1, 0, 5, None) == -1

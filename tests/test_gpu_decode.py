@@ -1,0 +1,135 @@
+"""GPU: split-KV paged decode and the LSE merge against the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from tests import cases
+from tests.gpu_util import assert_close, dev, device_cache, host, sm_scale
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def plc():
+    import paged_long_context_amd as m
+    return m
+
+
+def run_decode(plc, w, dtype, partition=0, cache=None, bt=None):
+    if cache is None:
+        cache, bt = device_cache(plc, w, dtype)
+    o, l = plc.attn_decode_paged(dev(w.q), cache, bt, dev(w.context_lens),
+                                 int(w.context_lens.max()), partition, sm_scale())
+    torch.cuda.synchronize()
+    return host(o), host(l)
+
+
+def oracle_decode(w, dtype):
+    return cases.oracle_attention(w, cases.oracle_cache(w, dtype), sm_scale())
+
+
+LENGTHS = [1, 15, 16, 17, 31, 32, 33, 100, 2047, 2048, 2049, 5000]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+@pytest.mark.parametrize("partition", [0, 16, 48, 512, 2048])
+def test_decode_lengths(plc, dtype, partition):
+    w = synthetic.generate(cases.spec(LENGTHS, [1] * len(LENGTHS), hq=8, hkv=1, seed=201))
+    o, l = run_decode(plc, w, dtype, partition)
+    ro, rl = oracle_decode(w, dtype)
+    assert_close(o, l, ro, rl, what="decode %s P=%d" % (dtype, partition))
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (4, 2), (16, 4), (32, 4), (16, 1)])
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+def test_decode_group_sizes(plc, hq, hkv, dtype):
+    w = synthetic.generate(cases.spec([700, 33, 4096], [1, 1, 1], hq=hq, hkv=hkv, seed=202))
+    o, l = run_decode(plc, w, dtype, 512)
+    ro, rl = oracle_decode(w, dtype)
+    assert_close(o, l, ro, rl, what="decode G=%d %s" % (hq // hkv, dtype))
+
+
+def test_decode_partials_then_merge_equals_decode(plc):
+    w = synthetic.generate(cases.spec([3000, 900, 17], [1, 1, 1], hq=8, hkv=1, seed=203))
+    cache, bt = device_cache(plc, w, "e4m3")
+    o1, l1 = run_decode(plc, w, "e4m3", 512, cache, bt)
+    op, lp = plc.attn_decode_partials(dev(w.q), cache, bt, dev(w.context_lens), 3000, 512, sm_scale())
+    o2, l2 = plc.lse_merge(op, lp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o2).reshape(o1.shape), o1)
+    assert np.array_equal(host(l2).reshape(l1.shape), l1)
+    # each partial against the oracle over its key window
+    c = cases.oracle_cache(w, "e4m3")
+    opn, lpn = host(op), host(lp)
+    for k in range(opn.shape[1]):
+        ro, rl = cases.oracle_attention(w, c, sm_scale(), key_begin=512 * k, key_end=512 * (k + 1))
+        ro = ro.reshape(-1, 128)
+        rl = rl.reshape(-1)
+        live = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(lpn[:, k]), live)
+        assert np.all(opn[~live, k] == 0)
+        if live.any():
+            assert_close(opn[live, k], lpn[live, k], ro[live], rl[live], what="part %d" % k)
+
+
+def test_lse_merge_against_oracle(plc):
+    rng = np.random.default_rng(204)
+    for rows, nparts, d in [(5, 1, 128), (64, 16, 128), (7, 300, 128), (3, 5, 64), (2, 9, 256)]:
+        o = rng.standard_normal((rows, nparts, d)).astype(np.float32)
+        l = (rng.standard_normal((rows, nparts)) * 30).astype(np.float32)
+        l[rng.random((rows, nparts)) < 0.2] = -np.inf
+        l[0, :] = -np.inf                      # an all-empty row
+        go, gl = plc.lse_merge(dev(o), dev(l))
+        ro, rl = oracle.lse_merge(o, l)
+        go, gl = host(go), host(gl)
+        assert np.all(go[0] == 0) and gl[0] == -np.inf
+        assert np.abs(go[1:] - ro[1:]).max() <= 1e-5
+        assert (np.abs(gl[1:] - rl[1:]) / np.maximum(1, np.abs(rl[1:]))).max() <= 1e-6
+
+
+def test_decode_is_deterministic_and_placement_independent(plc):
+    w = synthetic.generate(cases.spec([5000, 1234], [1, 1], hq=8, hkv=1, seed=205))
+    cache, bt = device_cache(plc, w, "e4m3")
+    o1, l1 = run_decode(plc, w, "e4m3", 1024, cache, bt)
+    o2, l2 = run_decode(plc, w, "e4m3", 1024, cache, bt)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    perm = np.random.default_rng(1).permutation(w.num_blocks).astype(np.int32)
+    bt2 = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    w2 = synthetic.Workload(**{**w.__dict__, "block_tables": bt2})
+    o3, l3 = run_decode(plc, w2, "e4m3", 1024)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+
+
+def test_decode_overflowing_logits(plc):
+    # logits far beyond fp16 range: q scaled so |s| reaches ~1e4
+    w = synthetic.generate(cases.spec([3000, 64], [1, 1], hq=8, hkv=1, seed=206, q_scale=900.0,
+                                      v_dist="uniform"))
+    for dtype in ["fp16", "e4m3", "int8"]:
+        o, l = run_decode(plc, w, dtype, 1024)
+        ro, rl = oracle_decode(w, dtype)
+        assert np.abs(rl).max() > 1000
+        assert_close(o, l, ro, rl, what="overflow %s" % dtype)
+
+
+@pytest.mark.parametrize("where", ["last", "block_edge", "partition_start", "first"])
+def test_decode_dominant_key(plc, where):
+    L = 4100
+    w = synthetic.generate(cases.spec([L], [1], hq=8, hkv=1, seed=207, v_dist="uniform"))
+    j = {"last": L - 1, "block_edge": 16 * 100 - 1, "partition_start": 2048, "first": 0}[where]
+    w.k[j, 0, :] = np.sign(w.q[0, 0].astype(np.float32)).astype(np.float16) * np.float16(2.0)
+    for dtype in ["fp16", "e4m3"]:
+        w.k_scale_head[:] = synthetic.e4m3_head_scales(w.k)
+        o, l = run_decode(plc, w, dtype, 1024)
+        ro, rl = oracle_decode(w, dtype)
+        assert_close(o, l, ro, rl, what="dominant %s %s" % (where, dtype))
+
+
+def test_decode_poison_does_not_leak(plc):
+    w = synthetic.generate(cases.spec([37, 5, 16], [1, 1, 1], hq=8, hkv=1, seed=208))
+    for dtype in ["fp16", "e4m3", "int8"]:
+        o, l = run_decode(plc, w, dtype, 0)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
