@@ -136,13 +136,35 @@ void orc_int8_encode_row(const uint16_t* x, int n, int8_t* codes, float* sigma_o
 /* KV append: write new tokens' K/V into their pages                   */
 /* ------------------------------------------------------------------ */
 
+/* E4M3 code of the fp16 value with bit pattern x after division by s: the
+ * encoder above applied once per distinct fp16 input (2 * Hkv tables of
+ * 65,536 entries, filled on first use), so long caches encode quickly. */
+typedef struct {
+    float scale;
+    uint8_t* codes;       /* [65536], NULL until built */
+} orc_e4m3_memo;
+
+static uint8_t orc_e4m3_memo_get(orc_e4m3_memo* m, float s, uint16_t x)
+{
+    if (!m->codes || m->scale != s) {
+        if (!m->codes)
+            m->codes = (uint8_t*)malloc(65536);
+        if (!m->codes)
+            abort();
+        m->scale = s;
+        for (int c = 0; c < 65536; ++c)
+            m->codes[c] = orc_e4m3_encode((float)orc_f16_value((uint16_t)c) / s);
+    }
+    return m->codes[x];
+}
+
 /*
  * Token t of the packed new K/V belongs to sequence b with
  * cu_new_lens[b] <= t < cu_new_lens[b+1]; its absolute position is
  * p = start_pos[b] + (t - cu_new_lens[b]); it goes to physical block
  * block_tables[b][p / block_size], slot p % block_size, layout
  * [num_blocks][num_kv_heads][block_size][head_dim].
- * Returns 0, or -1 when a target block is outside the pool.
+ * Returns 0, -1 when a target block is outside the pool, -2 without memory.
  */
 int orc_kv_append(int32_t kv_dtype,
                   const uint16_t* k_new, const uint16_t* v_new,
@@ -152,14 +174,25 @@ int orc_kv_append(int32_t kv_dtype,
                   const float* k_scale_head, const float* v_scale_head,
                   void* k_cache, void* v_cache, float* k_scale_tok, float* v_scale_tok)
 {
-    for (int b = 0; b < num_seqs; ++b) {
+    orc_e4m3_memo* memo = NULL;
+    if (kv_dtype == ORC_KV_E4M3) {
+        memo = (orc_e4m3_memo*)calloc(2 * (size_t)num_kv_heads, sizeof(orc_e4m3_memo));
+        if (!memo)
+            return -2;
+    }
+    int status = 0;
+    for (int b = 0; b < num_seqs && status == 0; ++b) {
         for (int t = cu_new_lens[b]; t < cu_new_lens[b + 1]; ++t) {
             int64_t p = (int64_t)start_pos[b] + (t - cu_new_lens[b]);
-            if (p / block_size >= max_blocks)
-                return -1;
+            if (p / block_size >= max_blocks) {
+                status = -1;
+                break;
+            }
             int32_t blk = block_tables[(int64_t)b * max_blocks + p / block_size];
-            if (blk < 0 || blk >= num_blocks)
-                return -1;
+            if (blk < 0 || blk >= num_blocks) {
+                status = -1;
+                break;
+            }
             int slot = (int)(p % block_size);
             for (int h = 0; h < num_kv_heads; ++h) {
                 const uint16_t* srcs[2] = {k_new + ((int64_t)t * num_kv_heads + h) * head_dim,
@@ -175,21 +208,24 @@ int orc_kv_append(int32_t kv_dtype,
                     } else if (kv_dtype == ORC_KV_E4M3) {
                         uint8_t* dst = (uint8_t*)dsts[w] + row * head_dim;
                         float s = head_scales[w][h];
-                        for (int d = 0; d < head_dim; ++d) {
-                            float xf = (float)orc_f16_value(x[d]);
-                            dst[d] = orc_e4m3_encode(xf / s);          /* fp32 division */
-                        }
+                        for (int d = 0; d < head_dim; ++d)   /* encode(x / s), fp32 division */
+                            dst[d] = orc_e4m3_memo_get(&memo[2 * h + w], s, x[d]);
                     } else if (kv_dtype == ORC_KV_INT8) {
                         int8_t* dst = (int8_t*)dsts[w] + row * head_dim;
                         orc_int8_encode_row(x, head_dim, dst, &tok_scales[w][row]);
                     } else {
-                        return -1;
+                        status = -1;
                     }
                 }
             }
         }
     }
-    return 0;
+    if (memo) {
+        for (int i = 0; i < 2 * num_kv_heads; ++i)
+            free(memo[i].codes);
+        free(memo);
+    }
+    return status;
 }
 
 /* ------------------------------------------------------------------ */
