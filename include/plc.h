@@ -133,9 +133,10 @@ int plc_attn_prefill_paged(const void* q, int32_t num_q_heads, const plc_kv_cach
 
 /*
  * Workspace bytes plc_attn_decode_paged / plc_attn_decode_partials need:
- * partial outputs fp32 [num_seqs * num_q_heads][nparts][head_dim] and partial
- * LSEs fp32 [num_seqs * num_q_heads][nparts], nparts =
- * ceil(max_context_len / partition), each region 256-byte aligned.
+ * partial outputs fp32 [num_seqs * num_q_heads][nparts][head_dim], partial
+ * LSEs fp32 [num_seqs * num_q_heads][nparts] (nparts =
+ * ceil(max_context_len / partition)) and int32 completion counters
+ * [num_seqs * num_q_heads], each region 256-byte aligned.
  * partition_tokens = 0 picks the default partition for max_context_len
  * (plc_decode_partition_tokens).
  */
@@ -156,8 +157,12 @@ int32_t plc_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
  *      partitions start at multiples of it; 0 = default.
  *  out (device): fp32 [num_seqs][num_q_heads][head_dim]; lse (device): fp32
  *      [num_seqs][num_q_heads].  A sequence of length 0 gives out 0, lse -inf.
- *  workspace (device): at least plc_decode_workspace_size(...) bytes.
- * Enqueues the partition kernel, then the merge.
+ *  workspace (device): at least plc_decode_workspace_size(...) bytes.  Its
+ *      counter region must be zero before the first call that uses it (a
+ *      zero-filled allocation does); every call leaves it zero again.  Calls
+ *      that share a workspace must not overlap in time.
+ * One kernel: each partition writes its partial state, and the last partition
+ * of each (sequence, KV head) to finish merges them into out / lse.
  */
 int plc_attn_decode_paged(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
                           const int32_t* block_tables, int32_t max_blocks,
@@ -167,11 +172,31 @@ int plc_attn_decode_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
                           void* stream);
 
 /*
+ * One decode step in one launch: append each sequence's step token and attend.
+ * Same result, bit for bit, as plc_kv_append_quant of k_new / v_new at
+ * position context_lens[b] - 1 (one token per sequence) followed by
+ * plc_attn_decode_paged with the same arguments.
+ *  k_new, v_new (device): fp16 [num_seqs][num_kv_heads][head_dim], the K/V of
+ *      the token each query belongs to.  A sequence with context 0 appends
+ *      nothing.
+ * The partition that holds position context_lens[b] - 1 writes the token
+ * before reading its pages; no other partition reads that page.
+ */
+int plc_attn_decode_append(const void* q, const void* k_new, const void* v_new,
+                           int32_t num_q_heads, const plc_kv_cache* kv,
+                           const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t max_context_len, int32_t partition_tokens, float sm_scale,
+                           float* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * First half of plc_attn_decode_paged: per-partition normalized outputs and
  * LSEs into the workspace, laid out as plc_lse_merge reads them (o_parts at
  * offset 0, lse_parts at *lse_parts_offset bytes, nparts in *nparts).
  * Partitions past a sequence's end hold o = 0, lse = -inf.  Lets a caller
  * merge partials from several sources (e.g. key shards on other devices).
+ * Does not touch the workspace's counters.
  */
 int plc_attn_decode_partials(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
                              const int32_t* block_tables, int32_t max_blocks,

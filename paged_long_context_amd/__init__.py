@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "PlcError", "KVCache", "kv_append_quant", "attn_prefill_paged", "attn_decode_paged",
-    "attn_decode_partials", "lse_merge", "decode_workspace_size", "decode_partition_tokens",
+    "attn_decode_append", "attn_decode_partials", "lse_merge", "decode_workspace_size", "decode_partition_tokens",
     "debug_e4m3_to_f16", "LIB_PATH", "KV_FP16", "KV_E4M3", "KV_INT8",
 ]
 
@@ -70,6 +70,9 @@ _lib.plc_decode_partition_tokens.argtypes = [_i32, _i32, _i32, _i32]
 _lib.plc_attn_decode_paged.restype = ctypes.c_int
 _lib.plc_attn_decode_paged.argtypes = [_P, _i32, _KV, _P, _i32, _P, _i32, _i32, _i32, _f32, _P, _P,
                                        _P, _sz, _P]
+_lib.plc_attn_decode_append.restype = ctypes.c_int
+_lib.plc_attn_decode_append.argtypes = [_P, _P, _P, _i32, _KV, _P, _i32, _P, _i32, _i32, _i32, _f32,
+                                        _P, _P, _P, _sz, _P]
 _lib.plc_attn_decode_partials.restype = ctypes.c_int
 _lib.plc_attn_decode_partials.argtypes = [_P, _i32, _KV, _P, _i32, _P, _i32, _i32, _i32, _f32, _P,
                                           _sz, ctypes.POINTER(_i32), ctypes.POINTER(_sz), _P]
@@ -225,7 +228,8 @@ def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, part
 def _workspace(q, num_seqs, Hq, D, max_context_len, partition_tokens, workspace):
     need = decode_workspace_size(num_seqs, Hq, D, max_context_len, partition_tokens)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        # zero-filled: the fused merge's completion counters start at zero
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8)
     return workspace
 
@@ -255,6 +259,37 @@ def attn_decode_paged(q: torch.Tensor, cache: KVCache, block_tables: torch.Tenso
                                       int(max_context_len), int(partition_tokens), float(sm_scale),
                                       _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                       _stream(stream)))
+    return out, lse
+
+
+def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: KVCache,
+                       block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                       partition_tokens: int = 0, sm_scale: Optional[float] = None, out=None,
+                       lse=None, workspace=None, stream=None):
+    """Append each sequence's step token (k_new / v_new fp16 [B][Hkv][D], at
+    position context_lens - 1) and decode, in one launch."""
+    B, Hq, D = q.shape
+    _need(q, "q", torch.float16)
+    _need(k_new, "k_new", torch.float16, (B, cache.num_kv_heads, D))
+    _need(v_new, "v_new", torch.float16, (B, cache.num_kv_heads, D))
+    _need(block_tables, "block_tables", torch.int32)
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    if block_tables.shape[0] != B:
+        raise ValueError("block_tables rows %d != num_seqs %d" % (block_tables.shape[0], B))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Hq, D))
+    _need(lse, "lse", torch.float32, (B, Hq))
+    workspace = _workspace(q, B, Hq, D, max_context_len, partition_tokens, workspace)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    _check(_lib.plc_attn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), Hq, cache.desc(),
+                                       _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                       B, int(max_context_len), int(partition_tokens),
+                                       float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)))
     return out, lse
 
 

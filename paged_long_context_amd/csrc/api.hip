@@ -96,11 +96,12 @@ int hip_status(hipError_t e, const char* what) {
 int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                           int32_t partition_tokens) {
     if (partition_tokens > 0) return partition_tokens;
-    // Enough partitions to give the 256 compute units several workgroups each,
-    // never shorter than 512 keys (merge traffic) nor longer than 4,096.
-    int64_t groups = (int64_t)num_seqs * num_kv_heads;
-    int32_t p = 4096;
-    while (p > 512 && groups * ((max_context_len + p - 1) / p) < 1024) p /= 2;
+    // The shortest power of two in [512, 8192] that keeps the grid within
+    // about one workgroup per compute unit (256 CUs): each workgroup then
+    // streams a long run of pages, and the merge reads few partials.
+    const int64_t groups = (int64_t)num_seqs * num_kv_heads;
+    int32_t p = 512;
+    while (p < 8192 && groups * ((max_context_len + p - 1) / p) > 256) p *= 2;
     return p;
 }
 
@@ -138,9 +139,15 @@ int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
     p.partition_tokens = P;
     p.nparts = nparts;
     p.qk_scale_log2 = sm_scale * 1.4426950408889634f;
+    const size_t o_bytes = align_up(rows * nparts * kv->head_dim * sizeof(float));
+    const size_t l_bytes = align_up(rows * nparts * sizeof(float));
     p.o_parts = static_cast<float*>(workspace);
-    p.lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           align_up(rows * nparts * kv->head_dim * sizeof(float)));
+    p.lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + o_bytes + l_bytes);
+    p.out = nullptr;
+    p.lse = nullptr;
+    p.k_new = nullptr;
+    p.v_new = nullptr;
     return PLC_OK;
 }
 
@@ -233,7 +240,10 @@ size_t plc_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
                           : resolve_partition(num_seqs, 1, max_context_len, 0);
     const int64_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
     const size_t rows = (size_t)num_seqs * num_q_heads;
-    return align_up(rows * nparts * head_dim * sizeof(float)) + align_up(rows * nparts * sizeof(float));
+    // partial outputs, partial LSEs, and one completion counter per
+    // (sequence, KV head) -- sized per query head, which is never fewer
+    return align_up(rows * nparts * head_dim * sizeof(float)) + align_up(rows * nparts * sizeof(float)) +
+           align_up(rows * sizeof(int32_t));
 }
 
 int plc_attn_decode_partials(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
@@ -249,6 +259,7 @@ int plc_attn_decode_partials(const void* q, int32_t num_q_heads, const plc_kv_ca
     if (nparts) *nparts = p.nparts;
     if (lse_parts_offset)
         *lse_parts_offset = (size_t)(reinterpret_cast<char*>(p.lse_parts) - static_cast<char*>(workspace));
+    p.counters = nullptr;                              // partials only: no merge
     return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)),
                       "decode partition launch");
 }
@@ -263,11 +274,30 @@ int plc_attn_decode_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
                           max_context_len, partition_tokens, sm_scale, workspace, workspace_bytes, &p);
     if (rc) return rc;
     if (!out || !lse) return fail(PLC_ERR_INVALID_ARG, "out / lse is NULL");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((rc = hip_status(plc::launch_decode_partials(p, s), "decode partition launch"))) return rc;
-    return hip_status(plc::launch_lse_merge(p.o_parts, p.lse_parts, num_seqs * num_q_heads, p.nparts,
-                                            kv->head_dim, out, lse, s),
-                      "lse merge launch");
+    p.out = out;                                       // the last partition of each group merges
+    p.lse = lse;
+    return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)),
+                      "decode launch");
+}
+
+int plc_attn_decode_append(const void* q, const void* k_new, const void* v_new,
+                           int32_t num_q_heads, const plc_kv_cache* kv,
+                           const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                           int32_t partition_tokens, float sm_scale, float* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    plc::DecodeParams p;
+    int rc = decode_setup(q, num_q_heads, kv, block_tables, max_blocks, context_lens, num_seqs,
+                          max_context_len, partition_tokens, sm_scale, workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    if (!out || !lse) return fail(PLC_ERR_INVALID_ARG, "out / lse is NULL");
+    if (!k_new || !v_new) return fail(PLC_ERR_INVALID_ARG, "k_new / v_new is NULL");
+    p.out = out;
+    p.lse = lse;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)),
+                      "decode-append launch");
 }
 
 int plc_lse_merge(const float* o_parts, const float* lse_parts, int32_t rows, int32_t nparts,

@@ -34,7 +34,8 @@ template <int KV>
 struct Chunk {
     // K: lane (row i = l%16, group g = l/16) holds, for each page, the bytes of
     // token i at d = 64h + 16g + [0, 16) for h = 0, 1.
-    u32x4 k[2][(KV == KV_FP16) ? 4 : 2];
+    u32x4 k[2][(KV == KV_FP16) ? 1 : 2];            // E4M3/INT8 codes
+    f16x8 kh[2][(KV == KV_FP16) ? 4 : 1];           // FP16 values, already operands
     // V: eight tokens t(g, e) = 16*(e/4) + 4g + e%4, d = 8*(l%16) + [0, 8).
     u32x4 v16[(KV == KV_FP16) ? 8 : 1];
     u32x2 v8[(KV == KV_FP16) ? 1 : 8];
@@ -46,7 +47,7 @@ template <int KV, int NW>
 struct Decode {
     static constexpr int EB = ElemBytes<KV>::value;
 
-    __device__ static void load(Chunk<KV>& c, const DecodeParams& p, int kvh, int pb0, int pb1,
+    __device__ __forceinline__ static void load(Chunk<KV>& c, const DecodeParams& p, int kvh, int pb0, int pb1,
                                 bool has1, int lane) {
         const int g = lane >> 4, i = lane & 15;
         const int nb = p.kv.num_blocks;
@@ -64,8 +65,8 @@ struct Decode {
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int sub = 0; sub < 2; ++sub)
-                        c.k[pg][2 * h + sub] =
-                            *reinterpret_cast<const u32x4*>(kr + (64 * h + 16 * g + 8 * sub) * 2);
+                        c.kh[pg][2 * h + sub] =
+                            *reinterpret_cast<const f16x8*>(kr + (64 * h + 16 * g + 8 * sub) * 2);
             } else {
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
@@ -94,10 +95,10 @@ struct Decode {
     }
 
     // K of page pg as the four MFMA A operands (d-slots kc = 2h + sub).
-    __device__ static void k_operands(const Chunk<KV>& c, int pg, f16x8 out[4]) {
+    __device__ __forceinline__ static void k_operands(const Chunk<KV>& c, int pg, f16x8 out[4]) {
         if constexpr (KV == KV_FP16) {
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) out[kc] = __builtin_bit_cast(f16x8, c.k[pg][kc]);
+            for (int kc = 0; kc < 4; ++kc) out[kc] = c.kh[pg][kc];
         } else {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -108,16 +109,17 @@ struct Decode {
     }
 
     // V^T operands: vt[col] holds V[t(g, e)][8*(l%16) + col] for e = 0..7.
-    __device__ static void v_operands(const Chunk<KV>& c, f16x8 vt[8]) {
+    __device__ __forceinline__ static void v_operands(const Chunk<KV>& c, f16x8 vt[8]) {
         if constexpr (KV == KV_FP16) {
             // 16-bit transpose: pair (e, e+1) of column col = perm of dword col/2.
 #pragma unroll
             for (int col = 0; col < 8; ++col) {
                 const uint32_t sel = (col & 1) ? 0x07060302u : 0x05040100u;
-                u32x4 r;
-#pragma unroll
-                for (int pr = 0; pr < 4; ++pr)
-                    r[pr] = __builtin_amdgcn_perm(c.v16[2 * pr + 1][col >> 1], c.v16[2 * pr][col >> 1], sel);
+                const int w = col >> 1;
+                const u32x4 r = u32x4{__builtin_amdgcn_perm(c.v16[1][w], c.v16[0][w], sel),
+                                      __builtin_amdgcn_perm(c.v16[3][w], c.v16[2][w], sel),
+                                      __builtin_amdgcn_perm(c.v16[5][w], c.v16[4][w], sel),
+                                      __builtin_amdgcn_perm(c.v16[7][w], c.v16[6][w], sel)};
                 vt[col] = __builtin_bit_cast(f16x8, r);
             }
         } else {
@@ -144,28 +146,189 @@ struct Decode {
         }
     }
 
-    // Zero V of tokens that must not contribute (past the end, bad page): a
-    // zero weight times a NaN poison value would still be NaN
-    // (INT8: the token's scale too, which may be a NaN poison).
-    __device__ static void mask_v(Chunk<KV>& c, const bool ok[8]) {
+    // Zero V codes of tokens that must not contribute (past the end, bad
+    // page): a zero weight times a NaN poison value would still be NaN (INT8:
+    // the token's scale too, which may be a NaN poison).  FP16 masks the
+    // operands instead (mask_vt), leaving the loaded words untouched.
+    __device__ __forceinline__ static void mask_v(Chunk<KV>& c, const bool ok[8]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if constexpr (KV == KV_FP16) {
-                if (!ok[e]) c.v16[e] = u32x4{0, 0, 0, 0};
-            } else {
-                if (!ok[e]) c.v8[e] = u32x2{0, 0};
-            }
-            if constexpr (KV == KV_INT8) {
-                if (!ok[e]) c.vs[e >> 2][e & 3] = 0.0f;
-            }
+        for (int e = 0; e < 8; ++e) {          // selects, not branches: stays in registers
+            c.v8[e][0] = ok[e] ? c.v8[e][0] : 0u;
+            c.v8[e][1] = ok[e] ? c.v8[e][1] : 0u;
+            if constexpr (KV == KV_INT8) c.vs[e >> 2][e & 3] = ok[e] ? c.vs[e >> 2][e & 3] : 0.0f;
         }
     }
 };
 
+// Online-softmax state of one wave: lane (i, g) owns query head i.
+struct WaveState {
+    float m, l;                    // running max (log2 units), lane-partial sum
+    f32x4 acc[8];                  // O^T[d = 32g + 8r + c][head i] in acc[c][r]
+};
+
 template <int KV, int NW>
-__global__ __launch_bounds__(64 * NW) void decode_partials_kernel(DecodeParams p) {
+__device__ __forceinline__ void process_chunk(WaveState& st, Chunk<KV>& cur, const f16x8 qop[4],
+                                              float cscale, int ctok, int tok1, int g) {
+    using Dk = Decode<KV, NW>;
+    // validity of the lane's eight tokens t(g, e)
+    bool ok[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int pg = e >> 2;
+        ok[e] = (ctok + 16 * pg + 4 * g + (e & 3) < tok1) && ((cur.valid_blk >> pg) & 1);
+    }
+    const bool partial = (ctok + 32 > tok1) || (cur.valid_blk != 3);
+    if constexpr (KV != KV_FP16)
+        if (partial) Dk::mask_v(cur, ok);
+
+    // S^T = K Q^T per page: lane holds tokens 4g + r of page pg, head i.
+    float x[8];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+        f16x8 kop[4];
+        Dk::k_operands(cur, pg, kop);
+        f32x4 s = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) s = mfma16(kop[kc], qop[kc], s);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float sc = cscale;
+            if constexpr (KV == KV_INT8) sc *= cur.ks[pg][r];
+            x[4 * pg + r] = s[r] * sc;
+        }
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        x[e] = ok[e] ? x[e] : -__builtin_inff();
+        mx = fmaxf(mx, x[e]);
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    // m_new is -inf only while every key so far is masked; keep the state finite
+    const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+    const float alpha = fast_exp2(st.m - m_use);
+    float psum = 0.0f;
+    f16x8 pop;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float pe = fast_exp2(x[e] - m_use);
+        psum += pe;
+        if constexpr (KV == KV_INT8) pe *= cur.vs[e >> 2][e & 3] * 256.0f;
+        pop[e] = (f16)pe;
+    }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st.acc[c] *= alpha;
+    }
+    f16x8 vt[8];
+    Dk::v_operands(cur, vt);
+    if constexpr (KV == KV_FP16)
+        if (partial) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vt[c][e] = ok[e] ? vt[c][e] : (f16)0.0f;
+        }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st.acc[c] = mfma16(vt[c], pop, st.acc[c]);
+}
+
+// Merge the partitions of one (sequence, KV head) group; run by the workgroup
+// that finished last.  One pass over the partials, every thread holding
+// several 16-byte loads in flight: thread (sub, d4) owns columns 4*d4..+3 of
+// row j for the parts k = ks, ks + KS, ... of its subset and keeps a running
+// maximum; the subsets are then combined in a fixed order through LDS.
+// lds must hold 2 * NW * (32 * 4 + 2) floats.
+template <int NW>
+__device__ void merge_group(const DecodeParams& p, int64_t row0, int G, int nparts_b, int tid,
+                            float* lds) {
+    constexpr int NSUB = 64 * NW / 32;                  // 32-lane groups (one row slice each)
+    f32x4* s_acc = reinterpret_cast<f32x4*>(lds);       // [NSUB][32]
+    float* s_m = lds + NSUB * 32 * 4;                   // [NSUB]
+    float* s_w = s_m + NSUB;                            // [NSUB]
+    const int nparts = p.nparts;
+    const int sub = tid >> 5, d4 = tid & 31;
+    const int RP = G < NSUB ? G : NSUB;                  // rows per pass
+    const int KS = NSUB / RP;                            // part subsets per row
+    const float NEG = -__builtin_inff();
+    for (int j0 = 0; j0 < G; j0 += RP) {
+        const int j = j0 + sub % RP, ks = sub / RP;
+        const float* lp = p.lse_parts + (row0 + j) * nparts;
+        const f32x4* op = reinterpret_cast<const f32x4*>(p.o_parts + (row0 + j) * nparts * D) + d4;
+        f32x4 acc = f32x4{0, 0, 0, 0};
+        float m = NEG, wsum = 0.0f;                      // running max (natural log units)
+        int k = ks;
+        for (; k + 7 * KS < nparts_b; k += 8 * KS) {
+            float lk[8];
+            f32x4 ov[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                lk[u] = lp[k + u * KS];
+                ov[u] = op[(int64_t)(k + u * KS) * (D / 4)];
+            }
+            float mb = m;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) mb = fmaxf(mb, lk[u]);
+            if (mb != NEG) {
+                const float sc = fast_exp2((m - mb) * kLog2e);   // 0 while m is -inf
+                acc *= sc;
+                wsum *= sc;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float w = fast_exp2((lk[u] - mb) * kLog2e);
+                    wsum += w;
+                    acc += w * ov[u];
+                }
+                m = mb;
+            }
+        }
+        for (; k < nparts_b; k += KS) {
+            const float lk = lp[k];
+            const f32x4 ov = op[(int64_t)k * (D / 4)];
+            const float mb = fmaxf(m, lk);
+            if (mb != NEG) {
+                const float sc = fast_exp2((m - mb) * kLog2e);
+                const float w = fast_exp2((lk - mb) * kLog2e);
+                acc = acc * sc + w * ov;
+                wsum = wsum * sc + w;
+                m = mb;
+            }
+        }
+        s_acc[sub * 32 + d4] = acc;
+        if (d4 == 0) {
+            s_m[sub] = m;
+            s_w[sub] = wsum;
+        }
+        __syncthreads();
+        if (ks == 0) {
+            float M = NEG;
+            for (int t = 0; t < KS; ++t) M = fmaxf(M, s_m[sub + t * RP]);
+            f32x4 a = f32x4{0, 0, 0, 0};
+            float ws = 0.0f;
+            if (M != NEG)
+                for (int t = 0; t < KS; ++t) {
+                    const int o = sub + t * RP;
+                    const float sc = fast_exp2((s_m[o] - M) * kLog2e);
+                    a += sc * s_acc[o * 32 + d4];
+                    ws += sc * s_w[o];
+                }
+            const bool empty = !(ws > 0.0f);
+            reinterpret_cast<f32x4*>(p.out + (row0 + j) * D)[d4] = empty ? f32x4{0, 0, 0, 0} : a / ws;
+            if (d4 == 0) p.lse[row0 + j] = empty ? NEG : M + __builtin_logf(ws);
+        }
+        __syncthreads();
+    }
+}
+
+template <int KV, int NW>
+__global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     using Dk = Decode<KV, NW>;
     extern __shared__ float smem[];
+    __shared__ int s_last;
     const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -173,12 +336,30 @@ __global__ __launch_bounds__(64 * NW) void decode_partials_kernel(DecodeParams p
     const int Hq = p.num_q_heads, G = Hq / p.kv.num_kv_heads;
     // lengths beyond the host-stated bound are clamped so that no page id
     // outside the table is ever read
-    const int L = min(p.context_lens[b], p.max_context_len);
-    const int tok0 = part * p.partition_tokens;
+    const int P = p.partition_tokens;
+    const int blk0 = part * (P / BS);
+    const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
+    // The first segment's page ids do not depend on the sequence length:
+    // fetch them now, alongside the length (entries past the end are masked
+    // once the length is known; the index stays inside the table row).
+    const int tb0 = 2 * (wave + (lane >> 1) * NW) + (lane & 1);
+    const int tbl0 = bt[min(blk0 + tb0, p.max_blocks - 1)];
+    const int L = max(0, min(p.context_lens[b], p.max_context_len));
+    const int nparts_b = (L + P - 1) / P;
+    const int tok0 = part * P;
     const int64_t row0 = (int64_t)b * Hq + (int64_t)kvh * G;   // first query row of the group
     const int nparts = p.nparts;
 
-    if (tok0 >= L) {                                             // partition past the end
+    if (part >= nparts_b) {                                      // partition past the end
+        if (p.counters) {
+            // fused call: only a sequence with no key at all has work here
+            if (part == 0)
+                for (int idx = tid; idx < G * D; idx += 64 * NW) {
+                    p.out[(row0 + idx / D) * D + idx % D] = 0.0f;
+                    if (idx % D == 0) p.lse[row0 + idx / D] = -__builtin_inff();
+                }
+            return;
+        }
         for (int idx = tid; idx < G * D; idx += 64 * NW) {
             const int j = idx / D, d = idx % D;
             p.o_parts[((row0 + j) * nparts + part) * D + d] = 0.0f;
@@ -186,11 +367,40 @@ __global__ __launch_bounds__(64 * NW) void decode_partials_kernel(DecodeParams p
         }
         return;
     }
-    const int tok1 = min(tok0 + p.partition_tokens, L);
+    const int tok1 = min(tok0 + P, L);
     const int nblk = (tok1 - tok0 + BS - 1) / BS;
     const int nchunks = (nblk + 1) / 2;
-    const int blk0 = tok0 / BS;
-    const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
+
+    if (p.k_new != nullptr && part == (L - 1) / P) {
+        // Fused append: this partition holds the step's own token (position
+        // L - 1).  Quantize its K and V exactly as plc_kv_append_quant does,
+        // write them to their page, and let the stores complete before any
+        // wave of this workgroup loads that page.
+        if (tid < 32) {
+            const int which = tid >> 4, sl = tid & 15;
+            const int pos = L - 1;
+            const int pg = bt[pos / BS];
+            const f16x8 x = *reinterpret_cast<const f16x8*>(
+                static_cast<const f16*>(which ? p.v_new : p.k_new) + ((int64_t)b * p.kv.num_kv_heads + kvh) * D +
+                8 * sl);
+            if (pg >= 0 && pg < p.kv.num_blocks) {
+                const int64_t crow = ((int64_t)pg * p.kv.num_kv_heads + kvh) * BS + (pos % BS);
+                void* cache = const_cast<void*>(which ? p.kv.v : p.kv.k);
+                if constexpr (KV == KV_FP16) {
+                    *reinterpret_cast<f16x8*>(static_cast<f16*>(cache) + crow * D + 8 * sl) = x;
+                } else {
+                    float s = 1.0f, sigma = 0.0f;
+                    if constexpr (KV == KV_E4M3) s = (which ? p.kv.v_scale : p.kv.k_scale)[kvh];
+                    const u32x2 w = quantize_slice<KV>(x, s, sigma);
+                    *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(cache) + crow * D + 8 * sl) = w;
+                    if constexpr (KV == KV_INT8)
+                        if (sl == 0) const_cast<float*>(which ? p.kv.v_scale : p.kv.k_scale)[crow] = sigma;
+                }
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
 
     // Q^T operand: lane (i, g) holds head i, d = 64*(kc/2) + 16g + 8*(kc%2) + [0, 8).
     f16x8 qop[4];
@@ -212,107 +422,48 @@ __global__ __launch_bounds__(64 * NW) void decode_partials_kernel(DecodeParams p
     if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
     if constexpr (KV == KV_INT8) vscale = 1.0f / 256.0f;
 
-    float m_run = -__builtin_inff();
-    float l_run = 0.0f;
-    f32x4 acc[8];
+    WaveState st;
+    st.m = -__builtin_inff();
+    st.l = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = f32x4{0, 0, 0, 0};
+    for (int c = 0; c < 8; ++c) st.acc[c] = f32x4{0, 0, 0, 0};
 
-    // Page ids of this wave's chunks, 32 chunks per refill: lane 2k+pg holds
-    // the page of chunk (wave + k*NW), page pg.
-    int tbl = 0;
-    auto refill = [&](int it0) {
-        const int k = lane >> 1, pg = lane & 1;
-        const int ch = wave + (it0 + k) * NW;
-        const int blk = 2 * ch + pg;
-        tbl = (ch < nchunks && blk < nblk) ? bt[blk0 + blk] : -1;
-    };
-    auto page = [&](int it, int pg) {
-        return __builtin_amdgcn_readlane(tbl, 2 * (it & 31) + pg);
-    };
-
-    const int my_chunks = (wave < nchunks) ? (nchunks - wave + NW - 1) / NW : 0;
-    Chunk<KV> cur, nxt;
-    if (my_chunks > 0) {
-        refill(0);
-        const int ch = wave;
-        Dk::load(cur, p, kvh, page(0, 0), page(0, 1), 2 * ch + 1 < nblk, lane);
-    }
-    for (int it = 0; it < my_chunks; ++it) {
-        const int ch = wave + it * NW;
-        if (it + 1 < my_chunks) {
-            if (((it + 1) & 31) == 0) refill(it + 1);
-            const int chn = ch + NW;
-            Dk::load(nxt, p, kvh, page(it + 1, 0), page(it + 1, 1), 2 * chn + 1 < nblk, lane);
+    // The wave's chunks are walked in segments of at most 32 whose 64 page ids
+    // sit one per lane of a VGPR (read with readlane).  Inside a segment the
+    // next chunk is always in flight: the prefetch target is clamped to the
+    // segment's last chunk, so a load past the end re-reads data already
+    // loaded (cache hits) and no load is conditional -- which lets the
+    // compiler wait only for the chunk in use.
+    // The wave's chunks are interleaved with the other waves' (chunk wave +
+    // it*NW), so at any time the workgroup streams neighbouring pages.
+    const int my_chunks = wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;
+    for (int seg = 0; seg < my_chunks; seg += 32) {
+        const int segn = min(32, my_chunks - seg);
+        const int tch = wave + (seg + (lane >> 1)) * NW;      // chunk of this lane's page
+        const int tb = 2 * tch + (lane & 1);
+        const bool tok = lane < 2 * segn && tb < nblk;
+        const int tbl = !tok ? -1 : (seg == 0 ? tbl0 : bt[blk0 + tb]);
+        auto load = [&](Chunk<KV>& c, int k) __attribute__((always_inline)) {  // k: index in segment
+            const int kk = min(k, segn - 1);
+            const int ch = wave + (seg + kk) * NW;
+            Dk::load(c, p, kvh, __builtin_amdgcn_readlane(tbl, 2 * kk),
+                     __builtin_amdgcn_readlane(tbl, 2 * kk + 1), 2 * ch + 1 < nblk, lane);
+        };
+        // two buffers in ping-pong: the next chunk's loads are in flight while
+        // the current one is computed
+        Chunk<KV> ca, cb;
+        load(ca, 0);
+        for (int k = 0; k < segn; k += 2) {
+            load(cb, k + 1);
+            process_chunk<KV, NW>(st, ca, qop, cscale, tok0 + 32 * (wave + (seg + k) * NW), tok1, g);
+            if (k + 1 >= segn) break;
+            load(ca, k + 2);
+            process_chunk<KV, NW>(st, cb, qop, cscale, tok0 + 32 * (wave + (seg + k + 1) * NW), tok1, g);
         }
-        // validity of the lane's eight tokens t(g, e)
-        bool ok[8];
-        const int ctok = tok0 + 32 * ch;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int pg = e >> 2;
-            ok[e] = (ctok + 16 * pg + 4 * g + (e & 3) < tok1) && ((cur.valid_blk >> pg) & 1);
-        }
-        const bool partial = (ctok + 32 > tok1) || (cur.valid_blk != 3);
-        if (partial) Dk::mask_v(cur, ok);
-
-        // S^T = K Q^T per page: lane holds tokens 4g + r of page pg, head i.
-        float x[8];
-#pragma unroll
-        for (int pg = 0; pg < 2; ++pg) {
-            f16x8 kop[4];
-            Dk::k_operands(cur, pg, kop);
-            f32x4 s = f32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) s = mfma16(kop[kc], qop[kc], s);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float sc = cscale;
-                if constexpr (KV == KV_INT8) sc *= cur.ks[pg][r];
-                x[4 * pg + r] = s[r] * sc;
-            }
-        }
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            x[e] = ok[e] ? x[e] : -__builtin_inff();
-            mx = fmaxf(mx, x[e]);
-        }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        // m_new is -inf only while every key so far is masked (cannot happen
-        // for a valid page of a non-empty partition, but keep the state finite)
-        const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        float psum = 0.0f;
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pe = fast_exp2(x[e] - m_use);
-            psum += pe;
-            pv[e] = pe;
-            if constexpr (KV == KV_INT8) pv[e] *= cur.vs[e >> 2][e & 3] * 256.0f;
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc[c] *= alpha;
-        }
-        f16x8 pop;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pop[e] = (f16)pv[e];
-
-        f16x8 vt[8];
-        Dk::v_operands(cur, vt);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = mfma16(vt[c], pop, acc[c]);
-
-        if (it + 1 < my_chunks) cur = nxt;
     }
 
     // ---- merge the waves of the workgroup (fixed order) ----
+    float l_run = st.l;
     l_run += shfl_xor(l_run, 16);
     l_run += shfl_xor(l_run, 32);
     constexpr int AST = D + 4;                         // padded head stride (floats)
@@ -320,15 +471,15 @@ __global__ __launch_bounds__(64 * NW) void decode_partials_kernel(DecodeParams p
     float* s_l = smem + NW * 16;                       // [NW][16]
     float* s_acc = smem + NW * 32;                     // [NW][G][AST]
     if (g == 0) {
-        s_m[wave * 16 + i] = m_run;
+        s_m[wave * 16 + i] = st.m;
         s_l[wave * 16 + i] = l_run;
     }
     if (i < G) {
         float* dst = s_acc + ((int64_t)wave * G + i) * AST + 32 * g;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            f32x4 lo = f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-            f32x4 hi = f32x4{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+            f32x4 lo = f32x4{st.acc[0][r], st.acc[1][r], st.acc[2][r], st.acc[3][r]};
+            f32x4 hi = f32x4{st.acc[4][r], st.acc[5][r], st.acc[6][r], st.acc[7][r]};
             *reinterpret_cast<f32x4*>(dst + 8 * r) = lo;
             *reinterpret_cast<f32x4*>(dst + 8 * r + 4) = hi;
         }
@@ -349,19 +500,49 @@ __global__ __launch_bounds__(64 * NW) void decode_partials_kernel(DecodeParams p
             }
         }
         const bool empty = !(Lsum > 0.0f);
-        p.o_parts[((row0 + j) * nparts + part) * D + d] = empty ? 0.0f : O * vscale / Lsum;
-        if (d == 0)
-            p.lse_parts[(row0 + j) * nparts + part] =
-                empty ? -__builtin_inff() : (M + __builtin_log2f(Lsum)) * kLn2;
+        const float ov = empty ? 0.0f : O * vscale / Lsum;
+        const float lv = empty ? -__builtin_inff() : (M + __builtin_log2f(Lsum)) * kLn2;
+        float* od = p.o_parts + ((row0 + j) * nparts + part) * D + d;
+        float* ld = p.lse_parts + (row0 + j) * nparts + part;
+        if (p.counters) {
+            // agent-coherent (write-through) stores: another workgroup, possibly
+            // on another XCD, reads them without any L2 write-back here
+            __hip_atomic_store(od, ov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == 0) __hip_atomic_store(ld, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            *od = ov;
+            if (d == 0) *ld = lv;
+        }
     }
+    if (!p.counters) return;
+
+    // ---- fused merge: the group's last workgroup to finish combines the parts.
+    // Every thread's partial stores have completed before the counter moves
+    // (vmcnt drained, then the barrier); only the last workgroup invalidates
+    // its caches before reading the other workgroups' partials.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+        int* cnt = p.counters + (int64_t)b * p.kv.num_kv_heads + kvh;
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == nparts_b - 1);
+        if (s_last)                                   // leave the counter zeroed for the next call
+            __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    merge_group<NW>(p, row0, G, nparts_b, tid, smem);
 }
 
 template <int KV, int NW>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
     const int G = p.num_q_heads / p.kv.num_kv_heads;
-    const size_t lds = sizeof(float) * (NW * 32 + (size_t)NW * G * (D + 4));
+    // wave-merge buffers; the fused merge reuses the same space
+    const size_t lds = sizeof(float) * max((size_t)NW * 32 + (size_t)NW * G * (D + 4),
+                                           (size_t)2 * NW * (32 * 4 + 2));
     dim3 grid(p.nparts, p.kv.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((decode_partials_kernel<KV, NW>), grid, dim3(64 * NW), lds, s, p);
+    hipLaunchKernelGGL((paged_decode_kernel<KV, NW>), grid, dim3(64 * NW), lds, s, p);
     return hipGetLastError();
 }
 

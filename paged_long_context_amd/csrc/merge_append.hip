@@ -96,37 +96,15 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
     if constexpr (KV == KV_FP16) {
         if (ok) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(const_cast<void*>(
                     which ? p.kv.v : p.kv.k)) + crow * D + 8 * part) = raw;
-    } else if constexpr (KV == KV_E4M3) {
-        const float s = (which ? p.kv.v_scale : p.kv.k_scale)[h];
-        uint32_t w[2] = {0, 0};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t c = f32_to_e4m3((float)x[e] / s);
-            w[e >> 2] |= c << (8 * (e & 3));
-        }
-        if (ok) *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(const_cast<void*>(
-                    which ? p.kv.v : p.kv.k)) + crow * D + 8 * part) = u32x2{w[0], w[1]};
     } else {
-        float m = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf((float)x[e]));
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor(m, off));
-        const float sigma = m / 127.0f;
-        uint32_t w[2] = {0, 0};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float q = 0.0f;
-            if (sigma != 0.0f) {
-                q = __builtin_rintf((float)x[e] / sigma);
-                q = fminf(fmaxf(q, -127.0f), 127.0f);
-            }
-            w[e >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (e & 3));
-        }
+        float s = 1.0f, sigma = 0.0f;
+        if constexpr (KV == KV_E4M3) s = (which ? p.kv.v_scale : p.kv.k_scale)[h];
+        const u32x2 w = quantize_slice<KV>(x, s, sigma);
         if (ok) {
             *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(const_cast<void*>(
-                which ? p.kv.v : p.kv.k)) + crow * D + 8 * part) = u32x2{w[0], w[1]};
-            if (part == 0) const_cast<float*>(which ? p.kv.v_scale : p.kv.k_scale)[crow] = sigma;
+                which ? p.kv.v : p.kv.k)) + crow * D + 8 * part) = w;
+            if constexpr (KV == KV_INT8)
+                if (part == 0) const_cast<float*>(which ? p.kv.v_scale : p.kv.k_scale)[crow] = sigma;
         }
     }
 }

@@ -107,6 +107,15 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
     return code | sign;
 }
 
+// Quantize one 8-value slice of a 128-value K or V row held by 16 consecutive
+// lanes (lane l%16 owns values 8*(l%16)..+7).  E4M3: x / s in IEEE fp32, then
+// f32_to_e4m3.  INT8: sigma = max|x| / 127 over the row (a 16-lane reduction,
+// so all 16 lanes must call), codes = clamp(rint(x / sigma), -127, 127), an
+// all-zero row giving sigma 0 and zero codes.  Returns the 8 codes, low byte
+// first; sigma is written for INT8.
+template <int KV>
+__device__ __forceinline__ u32x2 quantize_slice(f16x8 x, float s, float& sigma);
+
 // ------------------------------------------------------------------ MFMA
 
 // D(16x16) += A(16x32) * B(32x16), f16 inputs, fp32 accumulate.
@@ -131,6 +140,32 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int KV>
+__device__ __forceinline__ u32x2 quantize_slice(f16x8 x, float s, float& sigma) {
+    uint32_t w[2] = {0, 0};
+    if constexpr (KV == KV_E4M3) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e >> 2] |= f32_to_e4m3((float)x[e] / s) << (8 * (e & 3));
+    } else {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf((float)x[e]));
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor(m, off));
+        sigma = m / 127.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float q = 0.0f;
+            if (sigma != 0.0f) {
+                q = __builtin_rintf((float)x[e] / sigma);
+                q = fminf(fmaxf(q, -127.0f), 127.0f);
+            }
+            w[e >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (e & 3));
+        }
+    }
+    return u32x2{w[0], w[1]};
+}
 
 template <typename T>
 __device__ __forceinline__ T load_nt(const T* p) {

@@ -32,6 +32,15 @@ struct DecodeParams {
     float qk_scale_log2;        // sm_scale * log2(e)
     float* o_parts;             // [B*Hq][nparts][D]
     float* lse_parts;           // [B*Hq][nparts]
+    // fused merge (NULL counters: partials only).  counters: int32 [B][Hkv],
+    // zero on entry, left zero; out fp32 [B][Hq][D], lse fp32 [B][Hq]
+    int32_t* counters;
+    float* out;
+    float* lse;
+    // fused append of each sequence's step token (position context_len - 1):
+    // f16 [B][Hkv][D] each, or NULL
+    const void* k_new;
+    const void* v_new;
 };
 
 hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s);

@@ -107,6 +107,7 @@ def test_workspace_size_formula(plc):
     # rows * nparts * D floats + rows * nparts floats, each 256-byte aligned
     rows, nparts = 8 * 8, 16
     want = ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
+    want += ((rows * 4 + 255) // 256) * 256
     assert plc.decode_workspace_size(8, 8, 128, 32768, 2048) == want
 
 
