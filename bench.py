@@ -353,6 +353,8 @@ def main():
         cache = caches[0]
         q = to_dev(w3.q)
         cu, ctx = to_dev(w3.cu_q_lens), to_dev(w3.context_lens)
+        kn, vn = w3.new_kv()                       # the chunk's own K/V, appended first
+        plc.kv_append_quant(cache, to_dev(kn), to_dev(vn), bt, cu, to_dev(w3.start_pos))
         out = torch.empty((8192, 8, 128), dtype=torch.float32, device="cuda")
         lse = torch.empty((8192, 8), dtype=torch.float32, device="cuda")
         sm = 1.0 / math.sqrt(128)
@@ -361,6 +363,7 @@ def main():
             plc.attn_prefill_paged(q, cache, bt, cu, ctx, 8192, 131072, sm, out=out, lse=lse)
         pre(0)
         torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all()), "c3 prefill output"
         n3 = max(3, min(20, K // 10))
         pw, pe = graph_time(pre, n3, reps=2)
         fl = prefill_flops(w3)

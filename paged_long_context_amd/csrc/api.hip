@@ -118,7 +118,8 @@ int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
     if (partition_tokens < 0 || partition_tokens % kv->block_size != 0)
         return fail(PLC_ERR_INVALID_ARG, "partition_tokens %d must be 0 or a multiple of block_size %d",
                     partition_tokens, kv->block_size);
-    if (!std::isfinite(sm_scale)) return fail(PLC_ERR_INVALID_ARG, "sm_scale is not finite");
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(PLC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
     const int32_t P = resolve_partition(num_seqs, kv->num_kv_heads, max_context_len, partition_tokens);
     const size_t need = plc_decode_workspace_size(num_seqs, num_q_heads, kv->head_dim,
                                                   max_context_len, P);
@@ -206,7 +207,8 @@ int plc_attn_prefill_paged(const void* q, int32_t num_q_heads, const plc_kv_cach
     if (total_q_tokens == 0 || max_q_len == 0) return PLC_OK;
     if (!q || !block_tables || !cu_q_lens || !context_lens || !out || !lse)
         return fail(PLC_ERR_INVALID_ARG, "q / block_tables / cu_q_lens / context_lens / out / lse is NULL");
-    if (!std::isfinite(sm_scale)) return fail(PLC_ERR_INVALID_ARG, "sm_scale is not finite");
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(PLC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
     plc::PrefillParams p;
     p.q = q;
     p.kv = view(kv);

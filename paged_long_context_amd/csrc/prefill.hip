@@ -27,8 +27,6 @@ namespace {
 constexpr int D = 128;
 constexpr int BS = 16;
 constexpr int KT = 64;                  // keys per tile
-constexpr int NWAVE = 4;
-constexpr int ROWS = 64 * NWAVE;        // query rows per workgroup
 constexpr int KSTR = D + 8;             // K row stride in LDS (halves)
 constexpr int VSTR = KT + 8;            // V^T row stride in LDS (halves)
 constexpr int KBUF = KT * KSTR;         // halves
@@ -146,11 +144,17 @@ __device__ __forceinline__ void stage_store(const Stage<KV>& st, f16* lk, f16* l
     }
 }
 
-template <int KV>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+// RT 32-row MFMA tiles per wave, NWAVE waves: 32 * RT * NWAVE query rows per
+// workgroup.
+template <int KV, int RT, int NWAVE>
+__global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
+    constexpr int ROWS = 32 * RT * NWAVE;
+    constexpr int NT = 64 * NWAVE;                   // threads
+    // K double-buffered, V triple-buffered: the last subtile's PV of tile j
+    // runs in iteration j + 1, while tile j + 2 is being staged
     __shared__ __attribute__((aligned(16))) f16 s_k[2][KBUF];
-    __shared__ __attribute__((aligned(16))) f16 s_v[2][VBUF];
-    __shared__ float s_ks[2][KT], s_vs[2][KT];
+    __shared__ __attribute__((aligned(16))) f16 s_v[3][VBUF];
+    __shared__ float s_ks[2][KT], s_vs[3][KT];
 
     const int tile = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -174,13 +178,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 
     // ---- Q operands: lane holds row l%32 of row-tile rt, d = 16kc + 8(l/32) + [0,8)
     const int h32 = lane >> 5, r32 = lane & 31;
-    f16x8 qop[2][8];
-    int rowpos[2];
-    int64_t rowid[2];
-    bool rowok[2];
+    f16x8 qop[RT][8];
+    int rowpos[RT];
+    int64_t rowid[RT];
+    bool rowok[RT];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int r = 64 * wave + 32 * rt + r32;
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = 32 * RT * wave + 32 * rt + r32;
         const int po = q0 + r / G;
         rowok[rt] = po < n;
         const int poc = rowok[rt] ? po : qlast;
@@ -196,11 +200,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
     if constexpr (KV == KV_INT8) vscale = 1.0f / 256.0f;
 
-    float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
-    float l_run[2] = {0.0f, 0.0f};
-    f32x16 acc[2][4];
+    float m_ref[RT], l_run[RT];                       // raw-score units
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+        m_ref[rt] = -__builtin_inff();
+        l_run[rt] = 0.0f;
+    }
+    const float grow_raw = (KV == KV_INT8) ? 0.0f : 8.0f / cscale;
+    f32x16 acc[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -216,103 +225,128 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
         return key < kend ? bt[key / BS] : -1;
     };
 
+    // the first 256 threads gather and convert the tiles
+    const bool stager = tid < 256;
     Stage<KV> st;
     int pk_next = page_k(0), pv_next[1] = {page_v(0)};
-    stage_load<KV>(st, p, kvh, 0, kend, pk_next, pv_next, tid);
+    if (stager) stage_load<KV>(st, p, kvh, 0, kend, pk_next, pv_next, tid);
     if (ntiles > 1) { pk_next = page_k(KT); pv_next[0] = page_v(KT); }
-    stage_store<KV>(st, s_k[0], s_v[0], s_ks[0], s_vs[0], tid);
+    if (stager) stage_store<KV>(st, s_k[0], s_v[0], s_ks[0], s_vs[0], tid);
     __syncthreads();
+
+    // Subtile pipeline: for each 32-key subtile, QK^T first, then the PV of
+    // the previous subtile (its MFMAs run while this subtile's softmax runs on
+    // the vector unit), then the softmax.  The previous subtile's P operands
+    // and V buffer are carried across iterations.
+    f16x8 pprev[RT][2];                               // [rt][half] of the pending subtile
+    int pv_buf = 0, pv_ks = 0;
+    bool pending = false;
+    auto pv = [&](int vb, int kss) __attribute__((always_inline)) {
+        const f16* lv = s_v[vb];
+        f16x8 va[4][2];                               // all V operands first
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                va[dt][hf] = *reinterpret_cast<const f16x8*>(lv + (32 * dt + r32) * VSTR + 8 * h32 +
+                                                             32 * kss + 16 * hf);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) acc[rt][dt] = mfma32(va[dt][hf], pprev[rt][hf], acc[rt][dt]);
+    };
 
     const int krow = key_of_row(r32);
     for (int j = 0; j < ntiles; ++j) {
         const int k0 = j * KT;
-        const int buf = j & 1;
+        const int kb = j & 1, vb = j % 3;
         if (j + 1 < ntiles) {
-            stage_load<KV>(st, p, kvh, k0 + KT, kend, pk_next, pv_next, tid);
+            if (stager) stage_load<KV>(st, p, kvh, k0 + KT, kend, pk_next, pv_next, tid);
             if (j + 2 < ntiles) { pk_next = page_k(k0 + 2 * KT); pv_next[0] = page_v(k0 + 2 * KT); }
         }
-        const f16* lk = s_k[buf];
-        const f16* lv = s_v[buf];
-
-        // S^T[key][row] for two 32-key subtiles and both row-tiles
-        f32x16 s[2][2];
+        const bool masked = j >= nfull;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+            // S^T[key][row] of this subtile for both row-tiles
+            f32x16 sc[RT];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[ks][rt][r] = 0.0f;
-            const f16* krp = lk + (32 * ks + krow) * KSTR + 8 * h32;
+                for (int r = 0; r < 16; ++r) sc[rt][r] = 0.0f;
+            const f16* krp = s_k[kb] + (32 * ks + krow) * KSTR + 8 * h32;
+            f16x8 ka[8];                              // all of the subtile's K operands first,
+#pragma unroll                                        // so the LDS latency is paid once
+            for (int kc = 0; kc < 8; ++kc) ka[kc] = *reinterpret_cast<const f16x8*>(krp + 16 * kc);
 #pragma unroll
-            for (int kc = 0; kc < 8; ++kc) {
-                const f16x8 a = *reinterpret_cast<const f16x8*>(krp + 16 * kc);
-                s[ks][0] = mfma32(a, qop[0][kc], s[ks][0]);
-                s[ks][1] = mfma32(a, qop[1][kc], s[ks][1]);
-            }
-        }
-        const bool masked = j >= nfull;
-        f16x8 pop[2][2][2];                          // [rt][ks][half]
+            for (int kc = 0; kc < 8; ++kc)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            float x[2][16];
-            float mx = -__builtin_inff();
+                for (int rt = 0; rt < RT; ++rt) sc[rt] = mfma32(ka[kc], qop[rt][kc], sc[rt]);
+            if (pending) pv(pv_buf, pv_ks);
+
+            f16x8 pnew[RT][2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int rt = 0; rt < RT; ++rt) {
+                // raw scores (INT8: times the key's scale), masked keys at -inf
+                float mx = -__builtin_inff();
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float v = s[ks][rt][r] * cscale;
-                    if constexpr (KV == KV_INT8)
-                        v *= s_ks[buf][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)];
+                    float v = sc[rt][r];
+                    if constexpr (KV == KV_INT8) v *= s_ks[kb][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)];
                     if (masked) {
                         const int key = k0 + 32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7);
                         v = (key <= rowpos[rt]) ? v : -__builtin_inff();
                     }
-                    x[ks][r] = v;
+                    sc[rt][r] = v;
                     mx = fmaxf(mx, v);
                 }
-            mx = fmaxf(mx, shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[rt], mx);
-            const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-            const float alpha = fast_exp2(m_run[rt] - m_use);
-            float psum = 0.0f;
+                mx = fmaxf(mx, shfl_xor(mx, 32));
+                // The reference maximum moves only when a row's maximum grew by
+                // more than grow_raw (2^8 in probability; 0 for INT8, whose P
+                // carries the value scale): the accumulators are rescaled
+                // rarely, not per subtile.
+                const bool grow = mx > m_ref[rt] + grow_raw;
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+                    const float m_new = grow ? mx : m_ref[rt];
+                    const float alpha = (m_ref[rt] == -__builtin_inff())
+                                            ? 0.0f
+                                            : fast_exp2((m_ref[rt] - m_new) * cscale);
+                    l_run[rt] *= alpha;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+                    for (int dt = 0; dt < 4; ++dt) acc[rt][dt] *= alpha;
+                    m_ref[rt] = m_new;
+                }
+                // p = 2^(c*s - c*m): one fma and one exp per score
+                const float moff = (m_ref[rt] == -__builtin_inff()) ? 0.0f : -m_ref[rt] * cscale;
+                float psum = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float pe = fast_exp2(x[ks][r] - m_use);
+                    float pe = fast_exp2(__builtin_fmaf(sc[rt][r], cscale, moff));
                     psum += pe;
                     if constexpr (KV == KV_INT8)
-                        pe *= s_vs[buf][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)] * 256.0f;
-                    pop[rt][ks][r >> 3][r & 7] = (f16)pe;
+                        pe *= s_vs[vb][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)] * 256.0f;
+                    pnew[rt][r >> 3][r & 7] = (f16)pe;
                 }
-            l_run[rt] = l_run[rt] * alpha + psum;
-            m_run[rt] = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) acc[rt][dt] *= alpha;
+                l_run[rt] += psum;
             }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) pprev[rt][hf] = pnew[rt][hf];
+            pv_buf = vb;
+            pv_ks = ks;
+            pending = true;
         }
-        // O^T[d][row] += V^T[d][key] P^T[key][row]
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            const f16* vrp = lv + (32 * dt + r32) * VSTR + 8 * h32;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const f16x8 a = *reinterpret_cast<const f16x8*>(vrp + 32 * ks + 16 * hf);
-                    acc[0][dt] = mfma32(a, pop[0][ks][hf], acc[0][dt]);
-                    acc[1][dt] = mfma32(a, pop[1][ks][hf], acc[1][dt]);
-                }
-        }
-        if (j + 1 < ntiles)
-            stage_store<KV>(st, s_k[buf ^ 1], s_v[buf ^ 1], s_ks[buf ^ 1], s_vs[buf ^ 1], tid);
+        if (j + 1 < ntiles && stager)
+            stage_store<KV>(st, s_k[kb ^ 1], s_v[(j + 1) % 3], s_ks[kb ^ 1], s_vs[(j + 1) % 3], tid);
         __syncthreads();
     }
+    if (pending) pv(pv_buf, pv_ks);
 
     // ---- epilogue: lanes l and l^32 hold halves of the same row's keys
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
         float l = l_run[rt] + shfl_xor(l_run[rt], 32);
         if (!rowok[rt]) continue;
         const float inv = vscale / l;
@@ -326,21 +360,30 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                                 acc[rt][dt][4 * a4 + 2], acc[rt][dt][4 * a4 + 3]} * inv;
                 *reinterpret_cast<f32x4*>(o + d) = v;
             }
-        if (h32 == 0) p.lse[rowid[rt]] = (m_run[rt] + __builtin_log2f(l)) * kLn2;
+        if (h32 == 0) p.lse[rowid[rt]] = (m_ref[rt] * cscale + __builtin_log2f(l)) * kLn2;
     }
 }
 
 }  // namespace
 
+#ifndef PLC_PREFILL_RT
+#define PLC_PREFILL_RT 1          // 32-row MFMA tiles per wave
+#endif
+#ifndef PLC_PREFILL_NWAVE
+#define PLC_PREFILL_NWAVE 8       // waves per workgroup
+#endif
+
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
+    constexpr int RT = PLC_PREFILL_RT, NW = PLC_PREFILL_NWAVE;
     const int G = p.num_q_heads / p.kv.num_kv_heads;
-    const int ppw = ROWS / G;
+    const int ppw = 32 * RT * NW / G;
     dim3 grid((p.max_q_len + ppw - 1) / ppw, p.kv.num_kv_heads, p.num_seqs);
     if (grid.x == 0) return hipSuccess;
+    const dim3 block(64 * NW);
     switch (p.kv.dtype) {
-    case KV_FP16: hipLaunchKernelGGL(prefill_kernel<KV_FP16>, grid, dim3(256), 0, s, p); break;
-    case KV_E4M3: hipLaunchKernelGGL(prefill_kernel<KV_E4M3>, grid, dim3(256), 0, s, p); break;
-    case KV_INT8: hipLaunchKernelGGL(prefill_kernel<KV_INT8>, grid, dim3(256), 0, s, p); break;
+    case KV_FP16: hipLaunchKernelGGL((prefill_kernel<KV_FP16, RT, NW>), grid, block, 0, s, p); break;
+    case KV_E4M3: hipLaunchKernelGGL((prefill_kernel<KV_E4M3, RT, NW>), grid, block, 0, s, p); break;
+    case KV_INT8: hipLaunchKernelGGL((prefill_kernel<KV_INT8, RT, NW>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
