@@ -18,6 +18,8 @@
 // O^T = V^T P^T on MFMA ("Wide QK / PV").  Tiles wholly below the chunk's first
 // position skip the causal mask; only the tiles at the diagonal apply it
 // (Layer 2 "Prefix / Causal-Tail Separation").
+#include <type_traits>
+
 #include "plc_device.h"
 #include "plc_internal.h"
 
@@ -232,15 +234,21 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
     if (stager) stage_load<KV>(st, p, kvh, 0, kend, pk_next, pv_next, tid);
     if (ntiles > 1) { pk_next = page_k(KT); pv_next[0] = page_v(KT); }
     if (stager) stage_store<KV>(st, s_k[0], s_v[0], s_ks[0], s_vs[0], tid);
+    for (int x = tid; x < VBUF / 8; x += NT)          // the zeroed V buffer the first PV reads
+        reinterpret_cast<f16x8*>(s_v[2])[x] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
     __syncthreads();
 
     // Subtile pipeline: for each 32-key subtile, QK^T first, then the PV of
     // the previous subtile (its MFMAs run while this subtile's softmax runs on
     // the vector unit), then the softmax.  The previous subtile's P operands
-    // and V buffer are carried across iterations.
+    // and V buffer are carried across iterations; before the first subtile
+    // they are zeros and a zeroed V buffer, so the PV step has no branch.
     f16x8 pprev[RT][2];                               // [rt][half] of the pending subtile
-    int pv_buf = 0, pv_ks = 0;
-    bool pending = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) pprev[rt][hf] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    int pv_buf = 2, pv_ks = 0;
     auto pv = [&](int vb, int kss) __attribute__((always_inline)) {
         const f16* lv = s_v[vb];
         f16x8 va[4][2];                               // all V operands first
@@ -259,17 +267,19 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
     };
 
     const int krow = key_of_row(r32);
-    for (int j = 0; j < ntiles; ++j) {
+    // One key tile; MASKED tiles (at the diagonal) compare each key with the
+    // row's position, the others skip the mask entirely.
+    auto run_tile = [&](auto mtag, int j) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
         const int k0 = j * KT;
         const int kb = j & 1, vb = j % 3;
         if (j + 1 < ntiles) {
             if (stager) stage_load<KV>(st, p, kvh, k0 + KT, kend, pk_next, pv_next, tid);
             if (j + 2 < ntiles) { pk_next = page_k(k0 + 2 * KT); pv_next[0] = page_v(k0 + 2 * KT); }
         }
-        const bool masked = j >= nfull;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            // S^T[key][row] of this subtile for both row-tiles
+            // S^T[key][row] of this subtile
             f32x16 sc[RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
             for (int kc = 0; kc < 8; ++kc)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) sc[rt] = mfma32(ka[kc], qop[rt][kc], sc[rt]);
-            if (pending) pv(pv_buf, pv_ks);
+            pv(pv_buf, pv_ks);
 
             f16x8 pnew[RT][2];
 #pragma unroll
@@ -294,7 +304,7 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
                 for (int r = 0; r < 16; ++r) {
                     float v = sc[rt][r];
                     if constexpr (KV == KV_INT8) v *= s_ks[kb][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)];
-                    if (masked) {
+                    if constexpr (MASKED) {
                         const int key = k0 + 32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7);
                         v = (key <= rowpos[rt]) ? v : -__builtin_inff();
                     }
@@ -307,7 +317,7 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
                 // carries the value scale): the accumulators are rescaled
                 // rarely, not per subtile.
                 const bool grow = mx > m_ref[rt] + grow_raw;
-                if (__builtin_amdgcn_ballot_w64(grow)) {
+                if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
                     const float m_new = grow ? mx : m_ref[rt];
                     const float alpha = (m_ref[rt] == -__builtin_inff())
                                             ? 0.0f
@@ -336,13 +346,15 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
                 for (int hf = 0; hf < 2; ++hf) pprev[rt][hf] = pnew[rt][hf];
             pv_buf = vb;
             pv_ks = ks;
-            pending = true;
         }
         if (j + 1 < ntiles && stager)
             stage_store<KV>(st, s_k[kb ^ 1], s_v[(j + 1) % 3], s_ks[kb ^ 1], s_vs[(j + 1) % 3], tid);
         __syncthreads();
-    }
-    if (pending) pv(pv_buf, pv_ks);
+    };
+    const int nunmasked = min(nfull, ntiles);
+    for (int j = 0; j < nunmasked; ++j) run_tile(std::false_type{}, j);
+    for (int j = nunmasked; j < ntiles; ++j) run_tile(std::true_type{}, j);
+    pv(pv_buf, pv_ks);
 
     // ---- epilogue: lanes l and l^32 hold halves of the same row's keys
 #pragma unroll
