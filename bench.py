@@ -5,8 +5,9 @@ Headline step (the workload the metric is quoted on): a decode step of a batch
 of 8 sequences with 32,768-token contexts, 8 query heads over 1 KV head,
 head_dim 128, E4M3 KV with fp32 per-head scales, 16-token pages scattered by a
 seeded permutation, split-KV partitions of 2,048 tokens merged by log-sum-exp.
-One step = append the step's new K/V token per sequence (kv_append_quant) +
-the partition kernel + the merge.  Eight copies of the cache (537 MB, twice
+One step = one launch of the decode kernel, which appends the step's new K/V
+token per sequence, runs every split-KV partition and merges the partials in
+the last workgroup of each (sequence, KV head).  Eight copies of the cache (537 MB, twice
 the 256 MB Infinity Cache) are rotated so every step reads its keys from HBM.
 Steps are captured in a HIP graph and replayed, so host launch overhead is
 not timed.
@@ -17,6 +18,10 @@ mixed decode (2 x 524,288 + 4 x 262,144) and the ragged 32-sequence decode in
 FP16 / E4M3 / INT8, and the CPU oracle timed on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu]
+
+Profiling aids (no bench line): --prefill-only runs and times just the chunked
+prefill; --copy-calibration runs a plain 256 MiB device copy five times, the
+known-size kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters.
 """
 import argparse
 import hashlib
@@ -53,6 +58,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="time only the headline step (no per-part graphs), e.g. under a profiler")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the chunked-prefill workload (for profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 256 MiB device copy 5 times and exit (counter calibration)")
     return ap.parse_args()
 
 
@@ -255,6 +264,44 @@ def cpu_baseline(w, dtype):
     return dt, threads
 
 
+def bench_prefill(plc, synthetic, specs, K):
+    """The 8,192-token chunked causal prefill after a 122,880-token prefix."""
+    # ---------------- C3 chunked prefill ----------------
+    log("generating c3 (8192 new after 122880 cached)")
+    w3 = synthetic.generate(specs["c3"])
+    caches, bt = build_cache(plc, w3, "e4m3", 1)
+    cache = caches[0]
+    q = to_dev(w3.q)
+    cu, ctx = to_dev(w3.cu_q_lens), to_dev(w3.context_lens)
+    kn, vn = w3.new_kv()                       # the chunk's own K/V, appended first
+    plc.kv_append_quant(cache, to_dev(kn), to_dev(vn), bt, cu, to_dev(w3.start_pos))
+    out = torch.empty((8192, 8, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((8192, 8), dtype=torch.float32, device="cuda")
+    sm = 1.0 / math.sqrt(128)
+
+    def pre(i):
+        plc.attn_prefill_paged(q, cache, bt, cu, ctx, 8192, 131072, sm, out=out, lse=lse)
+    pre(0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all()), "c3 prefill output"
+    n3 = max(3, min(20, K // 10))
+    pw, pe = graph_time(pre, n3, reps=2)
+    fl = prefill_flops(w3)
+    tf = fl / pe / 1e12
+    res = {
+        "workload": "c3: 8192 new tokens after a 122880-token cached prefix, 8 q / 1 kv, E4M3",
+        "tflops": round(tf, 2), "unit": "TFLOP/s", "us_per_call": round(pe * 1e6, 1),
+        "useful_flops": fl,
+        "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL, "achieved": round(tf, 2),
+                     "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / F16_MFMA_PEAK_TFLOPS, 4)},
+    }
+    log("c3 prefill %.1f us, %.1f TFLOP/s" % (pe * 1e6, tf))
+    del caches, cache, q, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def read_traffic(launch_bytes):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
     if it was taken on the current decode kernel source."""
@@ -281,6 +328,17 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     specs = synthetic.named_specs()
     K, W = args.steps, args.warmup
+    if args.copy_calibration:
+        x = torch.full((256 << 20,), 1, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log("copied 5 x 256 MiB")
+        return
+    if args.prefill_only:
+        print(json.dumps({"c3_prefill": bench_prefill(plc, synthetic, specs, K)}), flush=True)
+        return
 
     # ---------------- headline: C2 decode step ----------------
     log("generating c2 (8 x 32768, e4m3)")
@@ -346,39 +404,7 @@ def main():
 
     if not args.headline_only:
         extra = {}
-        # ---------------- C3 chunked prefill ----------------
-        log("generating c3 (8192 new after 122880 cached)")
-        w3 = synthetic.generate(specs["c3"])
-        caches, bt = build_cache(plc, w3, "e4m3", 1)
-        cache = caches[0]
-        q = to_dev(w3.q)
-        cu, ctx = to_dev(w3.cu_q_lens), to_dev(w3.context_lens)
-        kn, vn = w3.new_kv()                       # the chunk's own K/V, appended first
-        plc.kv_append_quant(cache, to_dev(kn), to_dev(vn), bt, cu, to_dev(w3.start_pos))
-        out = torch.empty((8192, 8, 128), dtype=torch.float32, device="cuda")
-        lse = torch.empty((8192, 8), dtype=torch.float32, device="cuda")
-        sm = 1.0 / math.sqrt(128)
-
-        def pre(i):
-            plc.attn_prefill_paged(q, cache, bt, cu, ctx, 8192, 131072, sm, out=out, lse=lse)
-        pre(0)
-        torch.cuda.synchronize()
-        assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all()), "c3 prefill output"
-        n3 = max(3, min(20, K // 10))
-        pw, pe = graph_time(pre, n3, reps=2)
-        fl = prefill_flops(w3)
-        tf = fl / pe / 1e12
-        extra["c3_prefill"] = {
-            "workload": "c3: 8192 new tokens after a 122880-token cached prefix, 8 q / 1 kv, E4M3",
-            "tflops": round(tf, 2), "unit": "TFLOP/s", "us_per_call": round(pe * 1e6, 1),
-            "useful_flops": fl,
-            "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL, "achieved": round(tf, 2),
-                         "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / F16_MFMA_PEAK_TFLOPS, 4)},
-        }
-        log("c3 prefill %.1f us, %.1f TFLOP/s" % (pe * 1e6, tf))
-        del caches, cache, q, out, lse
-        torch.cuda.empty_cache()
+        extra["c3_prefill"] = bench_prefill(plc, synthetic, specs, K)
         # ---------------- C4 / C5 decode ----------------
         for name, dtypes in (("c4", ["e4m3"]), ("c5", ["fp16", "e4m3", "int8"])):
             log("generating %s" % name)

@@ -1,15 +1,16 @@
 // Chunked causal prefill over the paged KV cache, for gfx950.
 //
-// Workgroup = 4 waves = 256 query rows of one KV head; a row is a (query
+// Workgroup = 8 waves = 256 query rows of one KV head; a row is a (query
 // position, query head) pair, positions outer, so the G query heads that read
 // one KV head share every K/V tile (1Cat-vLLM README, Layer 2 "GQA Multi-Head
-// Packing").  Each wave owns 64 rows as two 32-row MFMA tiles and keeps their
-// Q operands and O accumulators in registers for the whole key loop.
+// Packing").  Each wave owns one 32-row MFMA tile and keeps its Q operands and
+// O accumulators in registers for the whole key loop; at about 210 VGPRs two
+// waves share each SIMD, so one wave's softmax overlaps the other's MFMAs.
 //
-// Keys are walked in tiles of 64 (four 16-token pages).  Per tile the
-// workgroup gathers the pages' codes with 16- and 8-byte loads (one page id per
-// page), converts them to fp16 exactly and writes K as [key][d] and V already
-// transposed as [d][key] into one of two LDS buffers; the next tile's loads are
+// Keys are walked in tiles of 64 (four 16-token pages).  Per tile four of the
+// waves gather the pages' codes with 16- and 8-byte loads (one page id per
+// page), convert them to fp16 exactly and write K as [key][d] (two LDS
+// buffers) and V already transposed as [d][key] (three); the next tile's loads are
 // in flight while the current tile is computed (Layer 1 and the
 // "Software-Reconstructed Async" section describe the same goals with V100
 // means).  Each wave then forms S^T = K Q^T on 32x32x16 f16 MFMA with fp32
@@ -29,21 +30,29 @@ namespace {
 constexpr int D = 128;
 constexpr int BS = 16;
 constexpr int KT = 64;                  // keys per tile
-constexpr int KSTR = D + 8;             // K row stride in LDS (halves)
+constexpr int KSTR = D;                 // K row stride in LDS (halves), swizzled
 constexpr int VSTR = KT + 8;            // V^T row stride in LDS (halves)
 constexpr int KBUF = KT * KSTR;         // halves
 constexpr int VBUF = D * VSTR;          // halves
 
-// Which key of a 32-key subtile MFMA row rho of S^T holds: the swap of bits 2
-// and 3 makes the eight keys a lane owns for one PV step consecutive.
+// Which key MFMA row rho of S^T holds (within a 64-key tile): the swap of
+// bits 2 and 3 makes the eight keys a lane owns for one PV step consecutive.
+// K is stored in LDS in MFMA row order, so LDS row rho holds key
+// key_of_row(rho) (the map is its own inverse).
 __device__ __forceinline__ int key_of_row(int rho) {
-    return (rho & 0x13) | ((rho & 0x8) >> 1) | ((rho & 0x4) << 1);
+    return (rho & 0x33) | ((rho & 0x8) >> 1) | ((rho & 0x4) << 1);
 }
+
+// K rows are 256 bytes without padding; the 16-byte chunk c of row rho lives
+// at chunk slot c ^ 2(c >> 3) ^ (rho & 15).  Operand reads (lanes = 16
+// consecutive rows, one chunk) and staging writes (lanes = 4 rows x 4 chunks
+// 4q + i) then touch 16 distinct slots, so neither conflicts on LDS banks.
+__device__ __forceinline__ int k_slot(int c, int rho) { return c ^ (2 * (c >> 3)) ^ (rho & 15); }
 
 template <int KV>
 struct Stage {
-    // Per thread: K of key t>>2, d = 32*(t&3) + [0,32); V of keys 4*(t>>4) + [0,4),
-    // d = 8*(t&15) + [0,8).
+    // Per thread: K of key t>>2, d = 32*(t&3) + [0,32); V of keys 4*(t&15) + [0,4),
+    // d = 8*(t>>4) + [0,8).
     u32x4 k[(KV == KV_FP16) ? 4 : 2];
     u32x4 v16[(KV == KV_FP16) ? 4 : 1];
     u32x2 v8[(KV == KV_FP16) ? 1 : 4];
@@ -69,7 +78,7 @@ __device__ __forceinline__ void stage_load(Stage<KV>& st, const PrefillParams& p
             st.ks = ok ? p.kv.k_scale[((int64_t)pg_k * Hkv + kvh) * BS + (key & (BS - 1))] : 0.0f;
     }
     {   // V: four consecutive keys share one page (4 | 16)
-        const int key0 = k0 + 4 * (tid >> 4);
+        const int key0 = k0 + 4 * (tid & 15);
         const int pg = pg_v[0];
         const bool pgok = pg >= 0 && pg < p.kv.num_blocks;
         const int64_t pb = pgok ? pg : 0;
@@ -78,7 +87,7 @@ __device__ __forceinline__ void stage_load(Stage<KV>& st, const PrefillParams& p
             const int key = key0 + e;
             const bool ok = pgok && key < kend;
             const uint8_t* src =
-                vc + (((pb * Hkv + kvh) * BS + (key & (BS - 1))) * D + 8 * (tid & 15)) * EB;
+                vc + (((pb * Hkv + kvh) * BS + (key & (BS - 1))) * D + 8 * (tid >> 4)) * EB;
             if constexpr (KV == KV_FP16)
                 st.v16[e] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
             else
@@ -92,23 +101,28 @@ __device__ __forceinline__ void stage_load(Stage<KV>& st, const PrefillParams& p
 template <int KV>
 __device__ __forceinline__ void stage_store(const Stage<KV>& st, f16* lk, f16* lv, float* lks,
                                             float* lvs, int tid) {
-    {   // K -> [key][d]
-        f16* dst = lk + (tid >> 2) * KSTR + 32 * (tid & 3);
+    {   // K -> LDS row key_of_row(key), chunks 4q + [0,4) at their swizzled slots
+        const int rho = key_of_row(tid >> 2), q = tid & 3;
+        f16* dst = lk + rho * KSTR;
         if constexpr (KV == KV_FP16) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(dst + 8 * j) = st.k[j];
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x4*>(dst + 8 * k_slot(4 * q + j, rho)) = st.k[j];
         } else {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                *reinterpret_cast<f16x8*>(dst + 16 * j) = codes8_to_f16x8<KV>(st.k[j][0], st.k[j][1]);
-                *reinterpret_cast<f16x8*>(dst + 16 * j + 8) = codes8_to_f16x8<KV>(st.k[j][2], st.k[j][3]);
+                *reinterpret_cast<f16x8*>(dst + 8 * k_slot(4 * q + 2 * j, rho)) =
+                    codes8_to_f16x8<KV>(st.k[j][0], st.k[j][1]);
+                *reinterpret_cast<f16x8*>(dst + 8 * k_slot(4 * q + 2 * j + 1, rho)) =
+                    codes8_to_f16x8<KV>(st.k[j][2], st.k[j][3]);
             }
         }
         if constexpr (KV == KV_INT8)
             if ((tid & 3) == 0) lks[tid >> 2] = st.ks;
     }
-    {   // V -> [d][key]: row 8*(t&15) + col, keys 4*(t>>4) + [0,4)
-        f16* dst = lv + (8 * (tid & 15)) * VSTR + 4 * (tid >> 4);
+    {   // V -> [d][key]: row 8*(t>>4) + col, keys 4*(t&15) + [0,4); the 16 lanes
+        // of a write cover one row's 64 keys, so the writes do not conflict
+        f16* dst = lv + (8 * (tid >> 4)) * VSTR + 4 * (tid & 15);
         if constexpr (KV == KV_FP16) {
 #pragma unroll
             for (int col = 0; col < 8; ++col) {
@@ -139,9 +153,9 @@ __device__ __forceinline__ void stage_store(const Stage<KV>& st, f16* lk, f16* l
             }
         }
         if constexpr (KV == KV_INT8)
-            if ((tid & 15) == 0) {
+            if ((tid >> 4) == 0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lvs[4 * (tid >> 4) + e] = st.vs[e];
+                for (int e = 0; e < 4; ++e) lvs[4 * (tid & 15) + e] = st.vs[e];
             }
     }
 }
@@ -217,13 +231,13 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[rt][dt][r] = 0.0f;
 
-    // page ids: K staging thread reads key k0 + (t>>2), V staging keys k0 + 4(t>>4)
+    // page ids: K staging thread reads key k0 + (t>>2), V staging keys k0 + 4(t&15)
     auto page_k = [&](int k0) {
         const int key = k0 + (tid >> 2);
         return key < kend ? bt[key / BS] : -1;
     };
     auto page_v = [&](int k0) {
-        const int key = k0 + 4 * (tid >> 4);
+        const int key = k0 + 4 * (tid & 15);
         return key < kend ? bt[key / BS] : -1;
     };
 
@@ -266,7 +280,7 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
                 for (int rt = 0; rt < RT; ++rt) acc[rt][dt] = mfma32(va[dt][hf], pprev[rt][hf], acc[rt][dt]);
     };
 
-    const int krow = key_of_row(r32);
+    const int kslot = h32 ^ (r32 & 15);              // lane part of the K chunk slot
     // One key tile; MASKED tiles (at the diagonal) compare each key with the
     // row's position, the others skip the mask entirely.
     auto run_tile = [&](auto mtag, int j) __attribute__((always_inline)) {
@@ -285,10 +299,13 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sc[rt][r] = 0.0f;
-            const f16* krp = s_k[kb] + (32 * ks + krow) * KSTR + 8 * h32;
+            // MFMA row r32 is LDS row 32ks + r32; its chunk 2kc + h32 sits at
+            // slot (2kc ^ 2(kc >> 2)) ^ h32 ^ (r32 & 15)
+            const f16* krp = s_k[kb] + (32 * ks + r32) * KSTR;
             f16x8 ka[8];                              // all of the subtile's K operands first,
 #pragma unroll                                        // so the LDS latency is paid once
-            for (int kc = 0; kc < 8; ++kc) ka[kc] = *reinterpret_cast<const f16x8*>(krp + 16 * kc);
+            for (int kc = 0; kc < 8; ++kc)
+                ka[kc] = *reinterpret_cast<const f16x8*>(krp + 8 * ((2 * kc ^ 2 * (kc >> 2)) ^ kslot));
 #pragma unroll
             for (int kc = 0; kc < 8; ++kc)
 #pragma unroll
