@@ -108,9 +108,16 @@ def prefill_flops(w):
     return 4 * s.head_dim * s.num_q_heads * pairs
 
 
-def source_hash(name):
-    with open(os.path.join(ROOT, "paged_long_context_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+DECODE_SOURCES = ("decode.hip", "plc_device.h", "plc_internal.h")
+
+
+def source_hash(names):
+    """First 16 hex digits of the SHA-256 of the named kernel sources, concatenated."""
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "paged_long_context_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stream_ptr():
@@ -310,7 +317,7 @@ def read_traffic(launch_bytes):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != source_hash("decode.hip"):
+    if t.get("source_sha256_16") != source_hash(DECODE_SOURCES):
         return None
     return t.get("hbm_bytes_per_launch")
 

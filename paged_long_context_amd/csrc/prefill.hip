@@ -49,87 +49,92 @@ __device__ __forceinline__ int key_of_row(int rho) {
 // 4q + i) then touch 16 distinct slots, so neither conflicts on LDS banks.
 __device__ __forceinline__ int k_slot(int c, int rho) { return c ^ (2 * (c >> 3)) ^ (rho & 15); }
 
+// Staging: the first half of the workgroup's threads gathers a tile's K, the
+// second half its V, 256 threads each.  A K thread holds key t>>2,
+// d = 32(t&3) + [0,32); a V thread holds keys 4(t&15) + [0,4), d = 8(t>>4) + [0,8)
+// (t = thread index within its half).  Either way a thread carries 32 codes.
 template <int KV>
 struct Stage {
-    // Per thread: K of key t>>2, d = 32*(t&3) + [0,32); V of keys 4*(t&15) + [0,4),
-    // d = 8*(t>>4) + [0,8).
-    u32x4 k[(KV == KV_FP16) ? 4 : 2];
-    u32x4 v16[(KV == KV_FP16) ? 4 : 1];
-    u32x2 v8[(KV == KV_FP16) ? 1 : 4];
-    float ks, vs[4];
+    // K: raw[j] = d chunk j (16 B each).  V: FP16 raw[e] = key e; 8-bit codes
+    // raw[e>>1] holds key e in dwords 2(e&1) + [0,2).
+    u32x4 raw[(KV == KV_FP16) ? 4 : 2];
+    float sc[4];                                     // INT8 scales: K sc[0], V sc[0..3]
 };
 
+// The page id the thread's first key lives on, or -1 past the visible keys.
+__device__ __forceinline__ int stage_page(const int32_t* bt, bool is_k, int k0, int kend, int t) {
+    const int key = k0 + (is_k ? (t >> 2) : 4 * (t & 15));
+    return key < kend ? bt[key / BS] : -1;
+}
+
 template <int KV>
-__device__ __forceinline__ void stage_load(Stage<KV>& st, const PrefillParams& p, int kvh, int k0,
-                                           int kend, int pg_k, const int pg_v[1], int tid) {
+__device__ __forceinline__ void stage_load(Stage<KV>& st, const PrefillParams& p, bool is_k, int kvh,
+                                           int k0, int kend, int pg, int t) {
     constexpr int EB = (KV == KV_FP16) ? 2 : 1;
     const int Hkv = p.kv.num_kv_heads;
-    const uint8_t* kc = static_cast<const uint8_t*>(p.kv.k);
-    const uint8_t* vc = static_cast<const uint8_t*>(p.kv.v);
-    {   // K
-        const int key = k0 + (tid >> 2);
-        const bool ok = key < kend && pg_k >= 0 && pg_k < p.kv.num_blocks;
-        const int64_t rowb = (((int64_t)(ok ? pg_k : 0) * Hkv + kvh) * BS + (key & (BS - 1))) * D * EB;
-        const uint8_t* src = kc + rowb + 32 * (tid & 3) * EB;
+    const bool pgok = pg >= 0 && pg < p.kv.num_blocks;
+    const int64_t pb = pgok ? pg : 0;
+    if (is_k) {
+        const int key = k0 + (t >> 2);
+        const bool ok = pgok && key < kend;
+        const int64_t row = (pb * Hkv + kvh) * BS + (key & (BS - 1));
+        const uint8_t* src = static_cast<const uint8_t*>(p.kv.k) + (row * D + 32 * (t & 3)) * EB;
 #pragma unroll
         for (int j = 0; j < ((KV == KV_FP16) ? 4 : 2); ++j)
-            st.k[j] = ok ? *reinterpret_cast<const u32x4*>(src + 16 * j) : u32x4{0, 0, 0, 0};
-        if constexpr (KV == KV_INT8)
-            st.ks = ok ? p.kv.k_scale[((int64_t)pg_k * Hkv + kvh) * BS + (key & (BS - 1))] : 0.0f;
-    }
-    {   // V: four consecutive keys share one page (4 | 16)
-        const int key0 = k0 + 4 * (tid & 15);
-        const int pg = pg_v[0];
-        const bool pgok = pg >= 0 && pg < p.kv.num_blocks;
-        const int64_t pb = pgok ? pg : 0;
+            st.raw[j] = ok ? *reinterpret_cast<const u32x4*>(src + 16 * j) : u32x4{0, 0, 0, 0};
+        if constexpr (KV == KV_INT8) st.sc[0] = ok ? p.kv.k_scale[row] : 0.0f;
+    } else {
+        // four consecutive keys share one page (4 | 16)
+        const int key0 = k0 + 4 * (t & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int key = key0 + e;
             const bool ok = pgok && key < kend;
-            const uint8_t* src =
-                vc + (((pb * Hkv + kvh) * BS + (key & (BS - 1))) * D + 8 * (tid >> 4)) * EB;
-            if constexpr (KV == KV_FP16)
-                st.v16[e] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
-            else
-                st.v8[e] = ok ? *reinterpret_cast<const u32x2*>(src) : u32x2{0, 0};
-            if constexpr (KV == KV_INT8)
-                st.vs[e] = ok ? p.kv.v_scale[(pb * Hkv + kvh) * BS + (key & (BS - 1))] : 0.0f;
+            const int64_t row = (pb * Hkv + kvh) * BS + (key & (BS - 1));
+            const uint8_t* src = static_cast<const uint8_t*>(p.kv.v) + (row * D + 8 * (t >> 4)) * EB;
+            if constexpr (KV == KV_FP16) {
+                st.raw[e] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+            } else {
+                const u32x2 c = ok ? *reinterpret_cast<const u32x2*>(src) : u32x2{0, 0};
+                st.raw[e >> 1][2 * (e & 1)] = c[0];
+                st.raw[e >> 1][2 * (e & 1) + 1] = c[1];
+            }
+            if constexpr (KV == KV_INT8) st.sc[e] = ok ? p.kv.v_scale[row] : 0.0f;
         }
     }
 }
 
 template <int KV>
-__device__ __forceinline__ void stage_store(const Stage<KV>& st, f16* lk, f16* lv, float* lks,
-                                            float* lvs, int tid) {
-    {   // K -> LDS row key_of_row(key), chunks 4q + [0,4) at their swizzled slots
-        const int rho = key_of_row(tid >> 2), q = tid & 3;
+__device__ __forceinline__ void stage_store(const Stage<KV>& st, bool is_k, f16* lk, f16* lv,
+                                            float* lks, float* lvs, int t) {
+    if (is_k) {   // K -> LDS row key_of_row(key), chunks 4q + [0,4) at their swizzled slots
+        const int rho = key_of_row(t >> 2), q = t & 3;
         f16* dst = lk + rho * KSTR;
         if constexpr (KV == KV_FP16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<u32x4*>(dst + 8 * k_slot(4 * q + j, rho)) = st.k[j];
+                *reinterpret_cast<u32x4*>(dst + 8 * k_slot(4 * q + j, rho)) = st.raw[j];
         } else {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 *reinterpret_cast<f16x8*>(dst + 8 * k_slot(4 * q + 2 * j, rho)) =
-                    codes8_to_f16x8<KV>(st.k[j][0], st.k[j][1]);
+                    codes8_to_f16x8<KV>(st.raw[j][0], st.raw[j][1]);
                 *reinterpret_cast<f16x8*>(dst + 8 * k_slot(4 * q + 2 * j + 1, rho)) =
-                    codes8_to_f16x8<KV>(st.k[j][2], st.k[j][3]);
+                    codes8_to_f16x8<KV>(st.raw[j][2], st.raw[j][3]);
             }
         }
         if constexpr (KV == KV_INT8)
-            if ((tid & 3) == 0) lks[tid >> 2] = st.ks;
-    }
-    {   // V -> [d][key]: row 8*(t>>4) + col, keys 4*(t&15) + [0,4); the 16 lanes
-        // of a write cover one row's 64 keys, so the writes do not conflict
-        f16* dst = lv + (8 * (tid >> 4)) * VSTR + 4 * (tid & 15);
+            if ((t & 3) == 0) lks[t >> 2] = st.sc[0];
+    } else {      // V -> [d][key]: row 8(t>>4) + col, keys 4(t&15) + [0,4); the 16 lanes
+                  // of a write cover one row's 64 keys, so the writes do not conflict
+        f16* dst = lv + (8 * (t >> 4)) * VSTR + 4 * (t & 15);
         if constexpr (KV == KV_FP16) {
 #pragma unroll
             for (int col = 0; col < 8; ++col) {
                 const uint32_t sel = (col & 1) ? 0x07060302u : 0x05040100u;
                 u32x2 r;
-                r[0] = __builtin_amdgcn_perm(st.v16[1][col >> 1], st.v16[0][col >> 1], sel);
-                r[1] = __builtin_amdgcn_perm(st.v16[3][col >> 1], st.v16[2][col >> 1], sel);
+                r[0] = __builtin_amdgcn_perm(st.raw[1][col >> 1], st.raw[0][col >> 1], sel);
+                r[1] = __builtin_amdgcn_perm(st.raw[3][col >> 1], st.raw[2][col >> 1], sel);
                 *reinterpret_cast<u32x2*>(dst + col * VSTR) = r;
             }
         } else {
@@ -138,7 +143,8 @@ __device__ __forceinline__ void stage_store(const Stage<KV>& st, f16* lk, f16* l
                 f16x2 pr[2][4];
 #pragma unroll
                 for (int pp = 0; pp < 2; ++pp) {
-                    const uint32_t a = st.v8[2 * pp + 1][hf], b = st.v8[2 * pp][hf];
+                    // keys 2pp and 2pp + 1, dword hf of each
+                    const uint32_t a = st.raw[pp][2 + hf], b = st.raw[pp][hf];
                     const uint32_t p01 = __builtin_amdgcn_perm(a, b, 0x05010400u);
                     const uint32_t p23 = __builtin_amdgcn_perm(a, b, 0x07030602u);
                     pr[pp][0] = codes2_to_f16x2<KV, false>(p01);
@@ -153,9 +159,9 @@ __device__ __forceinline__ void stage_store(const Stage<KV>& st, f16* lk, f16* l
             }
         }
         if constexpr (KV == KV_INT8)
-            if ((tid >> 4) == 0) {
+            if ((t >> 4) == 0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lvs[4 * (tid & 15) + e] = st.vs[e];
+                for (int e = 0; e < 4; ++e) lvs[4 * (t & 15) + e] = st.sc[e];
             }
     }
 }
@@ -231,23 +237,15 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[rt][dt][r] = 0.0f;
 
-    // page ids: K staging thread reads key k0 + (t>>2), V staging keys k0 + 4(t&15)
-    auto page_k = [&](int k0) {
-        const int key = k0 + (tid >> 2);
-        return key < kend ? bt[key / BS] : -1;
-    };
-    auto page_v = [&](int k0) {
-        const int key = k0 + 4 * (tid & 15);
-        return key < kend ? bt[key / BS] : -1;
-    };
-
-    // the first 256 threads gather and convert the tiles
-    const bool stager = tid < 256;
+    // waves 0-3 stage K, waves 4-7 stage V
+    static_assert(NT == 512, "staging assumes 256 K threads and 256 V threads");
+    const bool is_k = wave < NWAVE / 2;
+    const int st_t = tid & 255;
     Stage<KV> st;
-    int pk_next = page_k(0), pv_next[1] = {page_v(0)};
-    if (stager) stage_load<KV>(st, p, kvh, 0, kend, pk_next, pv_next, tid);
-    if (ntiles > 1) { pk_next = page_k(KT); pv_next[0] = page_v(KT); }
-    if (stager) stage_store<KV>(st, s_k[0], s_v[0], s_ks[0], s_vs[0], tid);
+    int pg_next = stage_page(bt, is_k, 0, kend, st_t);
+    stage_load<KV>(st, p, is_k, kvh, 0, kend, pg_next, st_t);
+    if (ntiles > 1) pg_next = stage_page(bt, is_k, KT, kend, st_t);
+    stage_store<KV>(st, is_k, s_k[0], s_v[0], s_ks[0], s_vs[0], st_t);
     for (int x = tid; x < VBUF / 8; x += NT)          // the zeroed V buffer the first PV reads
         reinterpret_cast<f16x8*>(s_v[2])[x] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
     __syncthreads();
@@ -288,8 +286,8 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
         const int k0 = j * KT;
         const int kb = j & 1, vb = j % 3;
         if (j + 1 < ntiles) {
-            if (stager) stage_load<KV>(st, p, kvh, k0 + KT, kend, pk_next, pv_next, tid);
-            if (j + 2 < ntiles) { pk_next = page_k(k0 + 2 * KT); pv_next[0] = page_v(k0 + 2 * KT); }
+            stage_load<KV>(st, p, is_k, kvh, k0 + KT, kend, pg_next, st_t);
+            if (j + 2 < ntiles) pg_next = stage_page(bt, is_k, k0 + 2 * KT, kend, st_t);
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -346,12 +344,14 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
                 }
                 // p = 2^(c*s - c*m): one fma and one exp per score
                 const float moff = (m_ref[rt] == -__builtin_inff()) ? 0.0f : -m_ref[rt] * cscale;
+                // l sums the fp32 p (summing the fp16-rounded weights would
+                // leave up to 2^-11 relative error in l on short rows)
                 float psum = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float pe = fast_exp2(__builtin_fmaf(sc[rt][r], cscale, moff));
                     psum += pe;
-                    if constexpr (KV == KV_INT8)
+                    if constexpr (KV == KV_INT8)   // P carries each key's value scale
                         pe *= s_vs[vb][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)] * 256.0f;
                     pnew[rt][r >> 3][r & 7] = (f16)pe;
                 }
@@ -364,8 +364,8 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
             pv_buf = vb;
             pv_ks = ks;
         }
-        if (j + 1 < ntiles && stager)
-            stage_store<KV>(st, s_k[kb ^ 1], s_v[(j + 1) % 3], s_ks[kb ^ 1], s_vs[(j + 1) % 3], tid);
+        if (j + 1 < ntiles)
+            stage_store<KV>(st, is_k, s_k[kb ^ 1], s_v[(j + 1) % 3], s_ks[kb ^ 1], s_vs[(j + 1) % 3], st_t);
         __syncthreads();
     };
     const int nunmasked = min(nfull, ntiles);
