@@ -44,139 +44,188 @@ __device__ __forceinline__ int key_of_row(int rho) {
 }
 
 // K rows are 256 bytes without padding; the 16-byte chunk c of row rho lives
-// at chunk slot c ^ 2(c >> 3) ^ (rho & 15).  Operand reads (lanes = 16
-// consecutive rows, one chunk) and staging writes (lanes = 4 rows x 4 chunks
-// 4q + i) then touch 16 distinct slots, so neither conflicts on LDS banks.
-__device__ __forceinline__ int k_slot(int c, int rho) { return c ^ (2 * (c >> 3)) ^ (rho & 15); }
+// at chunk slot h(c) ^ g(rho), h(c) = (c >> 1) | 8(c & 1),
+// g(rho) = (rho & 7) | 8((rho ^ rho >> 3) & 1).  Operand reads (lanes = 16
+// consecutive rows, one chunk) and staging writes (lanes = 2 rows x 8 chunks
+// 2q + i) then touch 16 distinct slots, so neither conflicts on LDS banks.
+__device__ __forceinline__ int k_row_key(int rho) { return (rho & 7) | (((rho ^ (rho >> 3)) & 1) << 3); }
+__device__ __forceinline__ int k_slot(int c, int rho) { return ((c >> 1) | ((c & 1) << 3)) ^ k_row_key(rho); }
 
-// Staging: the first half of the workgroup's threads gathers a tile's K, the
-// second half its V, 256 threads each.  A K thread holds key t>>2,
-// d = 32(t&3) + [0,32); a V thread holds keys 4(t&15) + [0,4), d = 8(t>>4) + [0,8)
-// (t = thread index within its half).  Either way a thread carries 32 codes.
+// V^T staging: thread group u = t >> 4 writes d rows 4 v_group(u) + [0,4); the
+// permutation puts the four 16-lane groups of a wave at row offsets 0, 32,
+// 16 and 48 words modulo 64, so a write covers all banks once.
+__device__ __forceinline__ int v_group(int u) { return (u & ~3) | ((u & 1) << 1) | ((u >> 1) & 1); }
+
+// Staging: every thread of the workgroup gathers 16 codes of a tile's K (key
+// t>>3, d = 16(t&7) + [0,16)) and 16 of its V (keys 4(t&15) + [0,4),
+// d = 4 v_group(t>>4) + [0,4)).  Keys past kend or on an invalid page are
+// zeroed when written to LDS; the loads themselves are always issued (from
+// page 0 when the key is not readable), so nothing waits on them early and
+// the loads in flight stay countable across the key loop.
 template <int KV>
 struct Stage {
-    // K: raw[j] = d chunk j (16 B each).  V: FP16 raw[e] = key e; 8-bit codes
-    // raw[e>>1] holds key e in dwords 2(e&1) + [0,2).
-    u32x4 raw[(KV == KV_FP16) ? 4 : 2];
-    float sc[4];                                     // INT8 scales: K sc[0], V sc[0..3]
+    static constexpr int NW = (KV == KV_FP16) ? 8 : 4;   // words of K, and of V
+    uint32_t k[NW];
+    uint32_t v[NW];                                  // 8-bit: v[e] = key e; fp16: v[2e + i]
+    float ks, vs[4];                                 // INT8 scales
+    uint32_t ok;                                     // bit 0: K key readable; bit 4 + e: V key e
 };
 
-// The page id the thread's first key lives on, or -1 past the visible keys.
-__device__ __forceinline__ int stage_page(const int32_t* bt, bool is_k, int k0, int kend, int t) {
-    const int key = k0 + (is_k ? (t >> 2) : 4 * (t & 15));
-    return key < kend ? bt[key / BS] : -1;
+// Per-thread constants of the staging addresses: a code's byte offset is
+// page * page_bytes + the thread's offset within a page (its keys' positions
+// in the page are the same for every tile, since tiles start on page bounds).
+struct StageAddr {
+    int64_t page_bytes;                              // Hkv * BS * D * elem bytes
+    int64_t k_off, v_off;                            // byte offsets within a page
+    int32_t page_rows;                               // Hkv * BS (INT8 scale rows per page)
+    int32_t ks_row, vs_row;                          // scale rows within a page
+};
+
+__device__ __forceinline__ int page_of(const int32_t* bt, int key, int kend) {
+    const int pg = bt[(uint32_t)min(key, kend - 1) / BS];   // unconditional read
+    return key < kend ? pg : -1;
 }
 
 template <int KV>
-__device__ __forceinline__ void stage_load(Stage<KV>& st, const PrefillParams& p, bool is_k, int kvh,
-                                           int k0, int kend, int pg, int t) {
-    constexpr int EB = (KV == KV_FP16) ? 2 : 1;
-    const int Hkv = p.kv.num_kv_heads;
+__device__ __forceinline__ void stage_load_k(Stage<KV>& st, const PrefillParams& p, const StageAddr& sa,
+                                             int key, int kend, int pg) {
     const bool pgok = pg >= 0 && pg < p.kv.num_blocks;
     const int64_t pb = pgok ? pg : 0;
-    if (is_k) {
-        const int key = k0 + (t >> 2);
-        const bool ok = pgok && key < kend;
-        const int64_t row = (pb * Hkv + kvh) * BS + (key & (BS - 1));
-        const uint8_t* src = static_cast<const uint8_t*>(p.kv.k) + (row * D + 32 * (t & 3)) * EB;
+    const uint8_t* src = static_cast<const uint8_t*>(p.kv.k) + pb * sa.page_bytes + sa.k_off;
 #pragma unroll
-        for (int j = 0; j < ((KV == KV_FP16) ? 4 : 2); ++j)
-            st.raw[j] = ok ? *reinterpret_cast<const u32x4*>(src + 16 * j) : u32x4{0, 0, 0, 0};
-        if constexpr (KV == KV_INT8) st.sc[0] = ok ? p.kv.k_scale[row] : 0.0f;
-    } else {
-        // four consecutive keys share one page (4 | 16)
-        const int key0 = k0 + 4 * (t & 15);
+    for (int j = 0; j < Stage<KV>::NW / 4; ++j) {
+        const u32x4 c = *reinterpret_cast<const u32x4*>(src + 16 * j);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int key = key0 + e;
-            const bool ok = pgok && key < kend;
-            const int64_t row = (pb * Hkv + kvh) * BS + (key & (BS - 1));
-            const uint8_t* src = static_cast<const uint8_t*>(p.kv.v) + (row * D + 8 * (t >> 4)) * EB;
-            if constexpr (KV == KV_FP16) {
-                st.raw[e] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
-            } else {
-                const u32x2 c = ok ? *reinterpret_cast<const u32x2*>(src) : u32x2{0, 0};
-                st.raw[e >> 1][2 * (e & 1)] = c[0];
-                st.raw[e >> 1][2 * (e & 1) + 1] = c[1];
-            }
-            if constexpr (KV == KV_INT8) st.sc[e] = ok ? p.kv.v_scale[row] : 0.0f;
-        }
+        for (int i = 0; i < 4; ++i) st.k[4 * j + i] = c[i];
     }
+    if constexpr (KV == KV_INT8) st.ks = p.kv.k_scale[pb * sa.page_rows + sa.ks_row];
+    st.ok = (st.ok & ~1u) | ((pgok && key < kend) ? 1u : 0u);
 }
 
+// key0 = the first of the thread's four V keys, which share one page (4 | 16)
 template <int KV>
-__device__ __forceinline__ void stage_store(const Stage<KV>& st, bool is_k, f16* lk, f16* lv,
-                                            float* lks, float* lvs, int t) {
-    if (is_k) {   // K -> LDS row key_of_row(key), chunks 4q + [0,4) at their swizzled slots
-        const int rho = key_of_row(t >> 2), q = t & 3;
-        f16* dst = lk + rho * KSTR;
+__device__ __forceinline__ void stage_load_v(Stage<KV>& st, const PrefillParams& p, const StageAddr& sa,
+                                             int key0, int kend, int pg) {
+    constexpr int EB = (KV == KV_FP16) ? 2 : 1;
+    const bool pgok = pg >= 0 && pg < p.kv.num_blocks;
+    const int64_t pb = pgok ? pg : 0;
+    const uint8_t* src = static_cast<const uint8_t*>(p.kv.v) + pb * sa.page_bytes + sa.v_off;
+    uint32_t okb = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
         if constexpr (KV == KV_FP16) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<u32x4*>(dst + 8 * k_slot(4 * q + j, rho)) = st.raw[j];
+            const u32x2 c = *reinterpret_cast<const u32x2*>(src + e * D * EB);
+            st.v[2 * e] = c[0];
+            st.v[2 * e + 1] = c[1];
         } else {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                *reinterpret_cast<f16x8*>(dst + 8 * k_slot(4 * q + 2 * j, rho)) =
-                    codes8_to_f16x8<KV>(st.raw[j][0], st.raw[j][1]);
-                *reinterpret_cast<f16x8*>(dst + 8 * k_slot(4 * q + 2 * j + 1, rho)) =
-                    codes8_to_f16x8<KV>(st.raw[j][2], st.raw[j][3]);
-            }
+            st.v[e] = *reinterpret_cast<const uint32_t*>(src + e * D * EB);
         }
-        if constexpr (KV == KV_INT8)
-            if ((t & 3) == 0) lks[t >> 2] = st.sc[0];
-    } else {      // V -> [d][key]: row 8(t>>4) + col, keys 4(t&15) + [0,4); the 16 lanes
-                  // of a write cover one row's 64 keys, so the writes do not conflict
-        f16* dst = lv + (8 * (t >> 4)) * VSTR + 4 * (t & 15);
-        if constexpr (KV == KV_FP16) {
-#pragma unroll
-            for (int col = 0; col < 8; ++col) {
-                const uint32_t sel = (col & 1) ? 0x07060302u : 0x05040100u;
-                u32x2 r;
-                r[0] = __builtin_amdgcn_perm(st.raw[1][col >> 1], st.raw[0][col >> 1], sel);
-                r[1] = __builtin_amdgcn_perm(st.raw[3][col >> 1], st.raw[2][col >> 1], sel);
-                *reinterpret_cast<u32x2*>(dst + col * VSTR) = r;
-            }
-        } else {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                f16x2 pr[2][4];
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    // keys 2pp and 2pp + 1, dword hf of each
-                    const uint32_t a = st.raw[pp][2 + hf], b = st.raw[pp][hf];
-                    const uint32_t p01 = __builtin_amdgcn_perm(a, b, 0x05010400u);
-                    const uint32_t p23 = __builtin_amdgcn_perm(a, b, 0x07030602u);
-                    pr[pp][0] = codes2_to_f16x2<KV, false>(p01);
-                    pr[pp][1] = codes2_to_f16x2<KV, true>(p01);
-                    pr[pp][2] = codes2_to_f16x2<KV, false>(p23);
-                    pr[pp][3] = codes2_to_f16x2<KV, true>(p23);
-                }
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    *reinterpret_cast<f16x4*>(dst + (4 * hf + c) * VSTR) =
-                        f16x4{pr[0][c][0], pr[0][c][1], pr[1][c][0], pr[1][c][1]};
-            }
-        }
-        if constexpr (KV == KV_INT8)
-            if ((t >> 4) == 0) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) lvs[4 * (t & 15) + e] = st.sc[e];
-            }
+        if constexpr (KV == KV_INT8) st.vs[e] = p.kv.v_scale[pb * sa.page_rows + sa.vs_row + e];
+        okb |= ((pgok && key0 + e < kend) ? 1u : 0u) << e;
     }
+    st.ok = (st.ok & 1u) | (okb << 4);
 }
 
-// RT 32-row MFMA tiles per wave, NWAVE waves: 32 * RT * NWAVE query rows per
-// workgroup.
-template <int KV, int RT, int NWAVE>
-__global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
-    constexpr int ROWS = 32 * RT * NWAVE;
-    constexpr int NT = 64 * NWAVE;                   // threads
-    // K double-buffered, V triple-buffered: the last subtile's PV of tile j
-    // runs in iteration j + 1, while tile j + 2 is being staged
+// K -> LDS row key_of_row(key), chunks 2(t&7) + [0,2) at their swizzled slots
+template <int KV>
+__device__ __forceinline__ void stage_store_k(const Stage<KV>& st, f16* lk, float* lks, int t) {
+    const int rho = key_of_row(t >> 3), c0 = 2 * (t & 7);
+    const bool ok = st.ok & 1u;
+    uint32_t c[Stage<KV>::NW];
+#pragma unroll
+    for (int i = 0; i < Stage<KV>::NW; ++i) c[i] = ok ? st.k[i] : 0u;
+    f16* dst = lk + rho * KSTR;
+    if constexpr (KV == KV_FP16) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<u32x4*>(dst + 8 * k_slot(c0 + j, rho)) =
+                u32x4{c[4 * j], c[4 * j + 1], c[4 * j + 2], c[4 * j + 3]};
+    } else {
+        *reinterpret_cast<f16x8*>(dst + 8 * k_slot(c0, rho)) = codes8_to_f16x8<KV>(c[0], c[1]);
+        *reinterpret_cast<f16x8*>(dst + 8 * k_slot(c0 + 1, rho)) = codes8_to_f16x8<KV>(c[2], c[3]);
+    }
+    if constexpr (KV == KV_INT8)
+        if ((t & 7) == 0) lks[t >> 3] = ok ? st.ks : 0.0f;
+}
+
+// V -> [d][key]: rows 4 v_group(t>>4) + [0,4), keys 4(t&15) + [0,4)
+template <int KV>
+__device__ __forceinline__ void stage_store_v(const Stage<KV>& st, f16* lv, float* lvs, int t) {
+    f16* dst = lv + (4 * v_group(t >> 4)) * VSTR + 4 * (t & 15);
+    auto okey = [&](int e) { return (st.ok >> (4 + e)) & 1u; };
+    if constexpr (KV == KV_FP16) {
+        uint32_t w2[4][2];                           // key e's d pairs, zeroed if unreadable
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) w2[e][i] = okey(e) ? st.v[2 * e + i] : 0u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int w = c >> 1;                    // word of each key holding the d pair
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            u32x2 r;
+            r[0] = __builtin_amdgcn_perm(w2[1][w], w2[0][w], sel);
+            r[1] = __builtin_amdgcn_perm(w2[3][w], w2[2][w], sel);
+            *reinterpret_cast<u32x2*>(dst + c * VSTR) = r;
+        }
+    } else {
+        f16x2 pr[2][4];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            // keys 2pp and 2pp + 1: byte c of each is d0 + c
+            const uint32_t a = okey(2 * pp + 1) ? st.v[2 * pp + 1] : 0u;
+            const uint32_t b = okey(2 * pp) ? st.v[2 * pp] : 0u;
+            const uint32_t p01 = __builtin_amdgcn_perm(a, b, 0x05010400u);
+            const uint32_t p23 = __builtin_amdgcn_perm(a, b, 0x07030602u);
+            pr[pp][0] = codes2_to_f16x2<KV, false>(p01);
+            pr[pp][1] = codes2_to_f16x2<KV, true>(p01);
+            pr[pp][2] = codes2_to_f16x2<KV, false>(p23);
+            pr[pp][3] = codes2_to_f16x2<KV, true>(p23);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<f16x4*>(dst + c * VSTR) = f16x4{pr[0][c][0], pr[0][c][1], pr[1][c][0], pr[1][c][1]};
+    }
+    if constexpr (KV == KV_INT8)
+        if ((t >> 4) == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lvs[4 * (t & 15) + e] = okey(e) ? st.vs[e] : 0.0f;
+        }
+}
+
+// Materialises v in registers at this point: arithmetic that produces v
+// cannot be sunk past it (a workgroup barrier orders memory only, so the
+// compiler may otherwise move the softmax into the next MFMA phase).
+template <typename T>
+__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
+
+// Phase barrier: every wave of the workgroup; the scheduler moves nothing
+// across it, so the MFMA and VALU phases stay as written.
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// 8 waves x 32 query rows.  The waves form two groups, 0-3 and 4-7, so each
+// SIMD holds one wave of each.  A step is one 32-key subtile in two phases:
+// the MFMA phase (the previous subtile's V operands from LDS, S = K Q^T of
+// this subtile, O += V^T P^T of the previous one, and the staging of the next
+// tile's K or V between those MFMAs) and the VALU phase (this subtile's online
+// softmax and the next subtile's K operands from LDS).  Both groups thus read
+// LDS in every phase, which a single wave per SIMD cannot saturate.  Group 4-7 starts one barrier late, so while one
+// group runs its MFMA phase the other runs its VALU phase and the two waves
+// of a SIMD keep the matrix core and the vector unit busy together.
+//
+// Global phase g is the span between the g-th and (g+1)-th barrier after the
+// first tile is staged.  Group 0-3 runs the MFMA phase of step i in phase 2i
+// and its VALU phase in 2i+1; group 4-7 runs them in 2i+1 and 2i+2.
+template <int KV>
+__global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
+    constexpr int ROWS = 256;
     __shared__ __attribute__((aligned(16))) f16 s_k[2][KBUF];
-    __shared__ __attribute__((aligned(16))) f16 s_v[3][VBUF];
-    __shared__ float s_ks[2][KT], s_vs[3][KT];
+    __shared__ __attribute__((aligned(16))) f16 s_v[2][VBUF];
+    __shared__ float s_ks[3][KT], s_vs[2][KT];     // INT8 key scales: three buffers (see below)
 
     const int tile = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -195,26 +244,26 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
     const int kend = base + qlast + 1;               // keys [0, kend) are visible to someone
     const int kfull = base + q0 + 1;                 // keys [0, kfull) are visible to every row
     const int ntiles = (kend + KT - 1) / KT;
-    const int nfull = kfull / KT;                    // tiles needing no mask
+    const int nfull = min(kfull / KT, ntiles);       // tiles needing no mask
     const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
+    const bool late = wave >= 4;                     // group 4-7: one phase behind
 
-    // ---- Q operands: lane holds row l%32 of row-tile rt, d = 16kc + 8(l/32) + [0,8)
+    // ---- Q operands: lane holds row l%32 of the wave's tile, d = 16kc + 8(l/32) + [0,8)
     const int h32 = lane >> 5, r32 = lane & 31;
-    f16x8 qop[RT][8];
-    int rowpos[RT];
-    int64_t rowid[RT];
-    bool rowok[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int r = 32 * RT * wave + 32 * rt + r32;
+    f16x8 qop[8];
+    int rowpos;
+    int64_t rowid;
+    bool rowok;
+    {
+        const int r = 32 * wave + r32;
         const int po = q0 + r / G;
-        rowok[rt] = po < n;
-        const int poc = rowok[rt] ? po : qlast;
-        rowpos[rt] = base + poc;
-        rowid[rt] = (int64_t)(qa + poc) * Hq + kvh * G + (r % G);
-        const f16* q = static_cast<const f16*>(p.q) + rowid[rt] * D + 8 * h32;
+        rowok = po < n;
+        const int poc = rowok ? po : qlast;
+        rowpos = base + poc;
+        rowid = (int64_t)(qa + poc) * Hq + kvh * G + (r % G);
+        const f16* q = static_cast<const f16*>(p.q) + rowid * D + 8 * h32;
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc) qop[rt][kc] = *reinterpret_cast<const f16x8*>(q + 16 * kc);
+        for (int kc = 0; kc < 8; ++kc) qop[kc] = *reinterpret_cast<const f16x8*>(q + 16 * kc);
     }
     float cscale = p.qk_scale_log2;
     if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
@@ -222,197 +271,210 @@ __global__ __launch_bounds__(64 * NWAVE) void prefill_kernel(PrefillParams p) {
     if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
     if constexpr (KV == KV_INT8) vscale = 1.0f / 256.0f;
 
-    float m_ref[RT], l_run[RT];                       // raw-score units
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        m_ref[rt] = -__builtin_inff();
-        l_run[rt] = 0.0f;
-    }
+    float m_ref = -__builtin_inff(), l_run = 0.0f;   // raw-score units
     const float grow_raw = (KV == KV_INT8) ? 0.0f : 8.0f / cscale;
-    f32x16 acc[RT][4];
+    f32x16 acc[4];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[rt][dt][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
 
-    // waves 0-3 stage K, waves 4-7 stage V
-    static_assert(NT == 512, "staging assumes 256 K threads and 256 V threads");
-    const bool is_k = wave < NWAVE / 2;
-    const int st_t = tid & 255;
+    // ---- staging.  K of tile T+1 is written to LDS during the MFMA phase of
+    // step 2T (phases 4T and 4T+1), V of tile T+1 during that of step 2T+1
+    // (4T+2, 4T+3), each interleaved with the MFMAs and followed by the loads
+    // of tile T+2.  Tile T's K operands are read in phases [4T-1, 4T+2], its V
+    // operands in [4T+2, 4T+5], its K and V scales (softmax) in [4T+1, 4T+4]:
+    // two K and V buffers suffice, the K scales need three.  Before the loop:
+    // tile 0 in LDS, tile 1 in registers, tile 2's page ids.
+    const int kkey = tid >> 3, vkey = 4 * (tid & 15);   // the thread's K key / first V key
+    StageAddr sa;
+    {
+        constexpr int EB = (KV == KV_FP16) ? 2 : 1;
+        const int Hkv = p.kv.num_kv_heads;
+        sa.page_rows = Hkv * BS;
+        sa.page_bytes = (int64_t)sa.page_rows * D * EB;
+        sa.ks_row = kvh * BS + (kkey & (BS - 1));
+        sa.vs_row = kvh * BS + (vkey & (BS - 1));
+        sa.k_off = ((int64_t)sa.ks_row * D + 16 * (tid & 7)) * EB;
+        sa.v_off = ((int64_t)sa.vs_row * D + 4 * v_group(tid >> 4)) * EB;
+    }
     Stage<KV> st;
-    int pg_next = stage_page(bt, is_k, 0, kend, st_t);
-    stage_load<KV>(st, p, is_k, kvh, 0, kend, pg_next, st_t);
-    if (ntiles > 1) pg_next = stage_page(bt, is_k, KT, kend, st_t);
-    stage_store<KV>(st, is_k, s_k[0], s_v[0], s_ks[0], s_vs[0], st_t);
-    for (int x = tid; x < VBUF / 8; x += NT)          // the zeroed V buffer the first PV reads
-        reinterpret_cast<f16x8*>(s_v[2])[x] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    st.ok = 0;
+    int pgk = page_of(bt, kkey, kend), pgv = page_of(bt, vkey, kend);
+    stage_load_k<KV>(st, p, sa, kkey, kend, pgk);
+    stage_load_v<KV>(st, p, sa, vkey, kend, pgv);
+    stage_store_k<KV>(st, s_k[0], s_ks[0], tid);
+    stage_store_v<KV>(st, s_v[0], s_vs[0], tid);
+    pgk = page_of(bt, KT + kkey, kend);
+    pgv = page_of(bt, KT + vkey, kend);
+    stage_load_k<KV>(st, p, sa, KT + kkey, kend, pgk);
+    stage_load_v<KV>(st, p, sa, KT + vkey, kend, pgv);
+    pgk = page_of(bt, 2 * KT + kkey, kend);
+    pgv = page_of(bt, 2 * KT + vkey, kend);
     __syncthreads();
 
-    // Subtile pipeline: for each 32-key subtile, QK^T first, then the PV of
-    // the previous subtile (its MFMAs run while this subtile's softmax runs on
-    // the vector unit), then the softmax.  The previous subtile's P operands
-    // and V buffer are carried across iterations; before the first subtile
-    // they are zeros and a zeroed V buffer, so the PV step has no branch.
-    f16x8 pprev[RT][2];                               // [rt][half] of the pending subtile
+    // K operands of one subtile: MFMA row r32 is LDS row 32ks + r32, whose
+    // chunk 2kc + h32 sits at slot kc ^ 8 h32 ^ k_row_key(r32)
+    const int kslot = (h32 << 3) ^ k_row_key(r32);
+    f16x8 ka[8];
+    auto load_k = [&](int kb, int ks) __attribute__((always_inline)) {
+        const f16* krp = s_k[kb] + (32 * ks + r32) * KSTR;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) pprev[rt][hf] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    int pv_buf = 2, pv_ks = 0;
-    auto pv = [&](int vb, int kss) __attribute__((always_inline)) {
+        for (int kc = 0; kc < 8; ++kc) ka[kc] = *reinterpret_cast<const f16x8*>(krp + 8 * (kc ^ kslot));
+    };
+    // P and V operands of the previous subtile (zero P before the first, on
+    // tile 0's V, which is finite) and its PV
+    f16x8 pprev[2] = {f16x8{0, 0, 0, 0, 0, 0, 0, 0}, f16x8{0, 0, 0, 0, 0, 0, 0, 0}};
+    f16x8 va[4][2];
+    auto load_v = [&](int vb, int kss) __attribute__((always_inline)) {
         const f16* lv = s_v[vb];
-        f16x8 va[4][2];                               // all V operands first
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
                 va[dt][hf] = *reinterpret_cast<const f16x8*>(lv + (32 * dt + r32) * VSTR + 8 * h32 +
                                                              32 * kss + 16 * hf);
+    };
+    auto pv = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) acc[rt][dt] = mfma32(va[dt][hf], pprev[rt][hf], acc[rt][dt]);
+            for (int hf = 0; hf < 2; ++hf) acc[dt] = mfma32(va[dt][hf], pprev[hf], acc[dt]);
     };
 
-    const int kslot = h32 ^ (r32 & 15);              // lane part of the K chunk slot
-    // One key tile; MASKED tiles (at the diagonal) compare each key with the
-    // row's position, the others skip the mask entirely.
-    auto run_tile = [&](auto mtag, int j) __attribute__((always_inline)) {
-        constexpr bool MASKED = decltype(mtag)::value;
-        const int k0 = j * KT;
-        const int kb = j & 1, vb = j % 3;
-        if (j + 1 < ntiles) {
-            stage_load<KV>(st, p, is_k, kvh, k0 + KT, kend, pg_next, st_t);
-            if (j + 2 < ntiles) pg_next = stage_page(bt, is_k, k0 + 2 * KT, kend, st_t);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            // S^T[key][row] of this subtile
-            f32x16 sc[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sc[rt][r] = 0.0f;
-            // MFMA row r32 is LDS row 32ks + r32; its chunk 2kc + h32 sits at
-            // slot (2kc ^ 2(kc >> 2)) ^ h32 ^ (r32 & 15)
-            const f16* krp = s_k[kb] + (32 * ks + r32) * KSTR;
-            f16x8 ka[8];                              // all of the subtile's K operands first,
-#pragma unroll                                        // so the LDS latency is paid once
-            for (int kc = 0; kc < 8; ++kc)
-                ka[kc] = *reinterpret_cast<const f16x8*>(krp + 8 * ((2 * kc ^ 2 * (kc >> 2)) ^ kslot));
-#pragma unroll
-            for (int kc = 0; kc < 8; ++kc)
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) sc[rt] = mfma32(ka[kc], qop[rt][kc], sc[rt]);
-            pv(pv_buf, pv_ks);
+    load_k(0, 0);
+    if (late) phase_barrier();
 
-            f16x8 pnew[RT][2];
+    // One step: subtile ks of tile T.  MASKED tiles (at the diagonal) compare
+    // each key with the row's position; the others skip the mask.
+    auto step = [&](auto mtag, auto kstag, int T) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
+        constexpr int ks = decltype(kstag)::value;
+        const int kb = T & 1;
+        // ---------------- MFMA phase: S of this subtile, PV of the previous;
+        // raised priority so the MFMAs win issue against the other wave's softmax
+        __builtin_amdgcn_s_setprio(2);
+        if constexpr (ks == 0) load_v(T > 0 ? (T - 1) & 1 : 0, 1);   // zero P before the first
+        else load_v(kb, 0);
+        f32x16 sc;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                // raw scores (INT8: times the key's scale), masked keys at -inf
-                float mx = -__builtin_inff();
+        for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float v = sc[rt][r];
-                    if constexpr (KV == KV_INT8) v *= s_ks[kb][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)];
-                    if constexpr (MASKED) {
-                        const int key = k0 + 32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7);
-                        v = (key <= rowpos[rt]) ? v : -__builtin_inff();
-                    }
-                    sc[rt][r] = v;
-                    mx = fmaxf(mx, v);
-                }
-                mx = fmaxf(mx, shfl_xor(mx, 32));
-                // The reference maximum moves only when a row's maximum grew by
-                // more than grow_raw (2^8 in probability; 0 for INT8, whose P
-                // carries the value scale): the accumulators are rescaled
-                // rarely, not per subtile.
-                const bool grow = mx > m_ref[rt] + grow_raw;
-                if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
-                    const float m_new = grow ? mx : m_ref[rt];
-                    const float alpha = (m_ref[rt] == -__builtin_inff())
-                                            ? 0.0f
-                                            : fast_exp2((m_ref[rt] - m_new) * cscale);
-                    l_run[rt] *= alpha;
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) acc[rt][dt] *= alpha;
-                    m_ref[rt] = m_new;
-                }
-                // p = 2^(c*s - c*m): one fma and one exp per score
-                const float moff = (m_ref[rt] == -__builtin_inff()) ? 0.0f : -m_ref[rt] * cscale;
-                // l sums the fp32 p (summing the fp16-rounded weights would
-                // leave up to 2^-11 relative error in l on short rows)
-                float psum = 0.0f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pe = fast_exp2(__builtin_fmaf(sc[rt][r], cscale, moff));
-                    psum += pe;
-                    if constexpr (KV == KV_INT8)   // P carries each key's value scale
-                        pe *= s_vs[vb][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)] * 256.0f;
-                    pnew[rt][r >> 3][r & 7] = (f16)pe;
-                }
-                l_run[rt] += psum;
+        for (int kc = 0; kc < 8; ++kc) sc = mfma32(ka[kc], qop[kc], sc);
+        pv();
+        {
+            // tile T+1 to LDS (past the last tile: zeros into a retired
+            // buffer), then tile T+2 into registers; branch-free, so that the
+            // scheduler can slot this work between the MFMAs
+            if constexpr (ks == 0) {
+                stage_store_k<KV>(st, s_k[kb ^ 1], s_ks[(T + 1) % 3], tid);
+                stage_load_k<KV>(st, p, sa, (T + 2) * KT + kkey, kend, pgk);
+                pgk = page_of(bt, (T + 3) * KT + kkey, kend);
+            } else {
+                stage_store_v<KV>(st, s_v[kb ^ 1], s_vs[kb ^ 1], tid);
+                stage_load_v<KV>(st, p, sa, (T + 2) * KT + vkey, kend, pgv);
+                pgv = page_of(bt, (T + 3) * KT + vkey, kend);
             }
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) pprev[rt][hf] = pnew[rt][hf];
-            pv_buf = vb;
-            pv_ks = ks;
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+            }
         }
-        if (j + 1 < ntiles)
-            stage_store<KV>(st, is_k, s_k[kb ^ 1], s_v[(j + 1) % 3], s_ks[kb ^ 1], s_vs[(j + 1) % 3], st_t);
-        __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
+        phase_barrier();
+
+        // ---------------- VALU phase: the next subtile's K operands, this
+        // subtile's softmax, its V operands, staging
+        if constexpr (ks == 0) load_k(kb, 1);
+        else load_k(kb ^ 1, 0);                     // past the last subtile: a harmless reread
+        const int k0 = T * KT + 32 * ks;
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // row r of this lane's scores holds key k0 + 16(r>>3) + 8 h32 + (r&7)
+            float v = sc[r];
+            if constexpr (KV == KV_INT8) v *= s_ks[T % 3][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)];
+            if constexpr (MASKED) {
+                const int key = k0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
+                v = (key <= rowpos) ? v : -__builtin_inff();
+            }
+            sc[r] = v;
+            mx = fmaxf(mx, v);
+        }
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        // The reference maximum moves only when a row's maximum grew by more
+        // than grow_raw (2^8 in probability; 0 for INT8, whose P carries the
+        // value scale): the accumulators are rescaled rarely, not per subtile.
+        const bool grow = mx > m_ref + grow_raw;
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = (m_ref == -__builtin_inff()) ? 0.0f : fast_exp2((m_ref - m_new) * cscale);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+            m_ref = m_new;
+        }
+        // p = 2^(c*s - c*m): one fma and one exp per score; l sums the fp32 p
+        // (summing the fp16-rounded weights would leave up to 2^-11 relative
+        // error in l on short rows)
+        const float moff = (m_ref == -__builtin_inff()) ? 0.0f : -m_ref * cscale;
+        float psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float pe = fast_exp2(__builtin_fmaf(sc[r], cscale, moff));
+            psum += pe;
+            if constexpr (KV == KV_INT8)   // P carries each key's value scale
+                pe *= s_vs[kb][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)] * 256.0f;
+            pprev[r >> 3][r & 7] = (f16)pe;
+        }
+        l_run += psum;
+        pin(pprev[0]);
+        pin(pprev[1]);
+        phase_barrier();
     };
-    const int nunmasked = min(nfull, ntiles);
-    for (int j = 0; j < nunmasked; ++j) run_tile(std::false_type{}, j);
-    for (int j = nunmasked; j < ntiles; ++j) run_tile(std::true_type{}, j);
-    pv(pv_buf, pv_ks);
+    using U = std::false_type;
+    using M = std::true_type;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    for (int T = 0; T < nfull; ++T) { step(U{}, S0{}, T); step(U{}, S1{}, T); }
+    for (int T = nfull; T < ntiles; ++T) { step(M{}, S0{}, T); step(M{}, S1{}, T); }
+    load_v((ntiles - 1) & 1, 1);
+    pv();
+    if (!late) phase_barrier();                      // equal barrier counts in both groups
 
     // ---- epilogue: lanes l and l^32 hold halves of the same row's keys
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        float l = l_run[rt] + shfl_xor(l_run[rt], 32);
-        if (!rowok[rt]) continue;
+    const float l = l_run + shfl_xor(l_run, 32);
+    if (rowok) {
         const float inv = vscale / l;
-        float* o = p.out + rowid[rt] * D;
+        float* o = p.out + rowid * D;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
                 const int d = 32 * dt + 8 * a4 + 4 * h32;
-                f32x4 v = f32x4{acc[rt][dt][4 * a4 + 0], acc[rt][dt][4 * a4 + 1],
-                                acc[rt][dt][4 * a4 + 2], acc[rt][dt][4 * a4 + 3]} * inv;
+                f32x4 v = f32x4{acc[dt][4 * a4 + 0], acc[dt][4 * a4 + 1], acc[dt][4 * a4 + 2],
+                                acc[dt][4 * a4 + 3]} * inv;
                 *reinterpret_cast<f32x4*>(o + d) = v;
             }
-        if (h32 == 0) p.lse[rowid[rt]] = (m_ref[rt] * cscale + __builtin_log2f(l)) * kLn2;
+        if (h32 == 0) p.lse[rowid] = (m_ref * cscale + __builtin_log2f(l)) * kLn2;
     }
 }
 
 }  // namespace
 
-#ifndef PLC_PREFILL_RT
-#define PLC_PREFILL_RT 1          // 32-row MFMA tiles per wave
-#endif
-#ifndef PLC_PREFILL_NWAVE
-#define PLC_PREFILL_NWAVE 8       // waves per workgroup
-#endif
-
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
-    constexpr int RT = PLC_PREFILL_RT, NW = PLC_PREFILL_NWAVE;
     const int G = p.num_q_heads / p.kv.num_kv_heads;
-    const int ppw = 32 * RT * NW / G;
+    const int ppw = 256 / G;                         // query positions per workgroup
     dim3 grid((p.max_q_len + ppw - 1) / ppw, p.kv.num_kv_heads, p.num_seqs);
     if (grid.x == 0) return hipSuccess;
-    const dim3 block(64 * NW);
+    const dim3 block(512);
     switch (p.kv.dtype) {
-    case KV_FP16: hipLaunchKernelGGL((prefill_kernel<KV_FP16, RT, NW>), grid, block, 0, s, p); break;
-    case KV_E4M3: hipLaunchKernelGGL((prefill_kernel<KV_E4M3, RT, NW>), grid, block, 0, s, p); break;
-    case KV_INT8: hipLaunchKernelGGL((prefill_kernel<KV_INT8, RT, NW>), grid, block, 0, s, p); break;
+    case KV_FP16: hipLaunchKernelGGL(prefill_kernel<KV_FP16>, grid, block, 0, s, p); break;
+    case KV_E4M3: hipLaunchKernelGGL(prefill_kernel<KV_E4M3>, grid, block, 0, s, p); break;
+    case KV_INT8: hipLaunchKernelGGL(prefill_kernel<KV_INT8>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
