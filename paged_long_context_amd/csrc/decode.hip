@@ -332,6 +332,11 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Chunk c of the partition goes to the wave with cw = c mod NW, cw =
+    // NW - 1 - wave: waves w and w + NW/2 share a SIMD and the second one
+    // issues behind the first, so the last chunk (the step's new token in a
+    // decode step) belongs to wave 0, which has slack for the append.
+    const int cw = NW - 1 - wave;
     const int g = lane >> 4, i = lane & 15;
     const int Hq = p.num_q_heads, G = Hq / p.kv.num_kv_heads;
     // lengths beyond the host-stated bound are clamped so that no page id
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     // The first segment's page ids do not depend on the sequence length:
     // fetch them now, alongside the length (entries past the end are masked
     // once the length is known; the index stays inside the table row).
-    const int tb0 = 2 * (wave + (lane >> 1) * NW) + (lane & 1);
+    const int tb0 = 2 * (cw + (lane >> 1) * NW) + (lane & 1);
     const int tbl0 = bt[min(blk0 + tb0, p.max_blocks - 1)];
     const int L = max(0, min(p.context_lens[b], p.max_context_len));
     const int nparts_b = (L + P - 1) / P;
@@ -371,13 +376,18 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     const int nblk = (tok1 - tok0 + BS - 1) / BS;
     const int nchunks = (nblk + 1) / 2;
 
-    if (p.k_new != nullptr && part == (L - 1) / P) {
+    const bool appends = p.k_new != nullptr && part == (L - 1) / P;     // uniform in the workgroup
+    if (appends && cw == ((L - 1 - tok0) / 32) % NW) {
         // Fused append: this partition holds the step's own token (position
-        // L - 1).  Quantize its K and V exactly as plc_kv_append_quant does,
-        // write them to their page, and let the stores complete before any
-        // wave of this workgroup loads that page.
-        if (tid < 32) {
-            const int which = tid >> 4, sl = tid & 15;
+        // L - 1) and this wave owns its chunk, the only one that reads that
+        // page.  Quantize the token's K and V exactly as plc_kv_append_quant
+        // does, write them to their page, and let the stores complete before
+        // this wave loads anything.  The codes of one page share no cache line
+        // with another page's, so the other waves need not wait; INT8 scale
+        // rows of neighbouring pages do share lines, so for INT8 the whole
+        // workgroup waits (below) before anyone loads.
+        if (lane < 32) {
+            const int which = lane >> 4, sl = lane & 15;
             const int pos = L - 1;
             const int pg = bt[pos / BS];
             const f16x8 x = *reinterpret_cast<const f16x8*>(
@@ -399,8 +409,9 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
             }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
     }
+    if constexpr (KV == KV_INT8)
+        if (appends) __syncthreads();
 
     // Q^T operand: lane (i, g) holds head i, d = 64*(kc/2) + 16g + 8*(kc%2) + [0, 8).
     f16x8 qop[4];
@@ -436,16 +447,16 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     // compiler wait only for the chunk in use.
     // The wave's chunks are interleaved with the other waves' (chunk wave +
     // it*NW), so at any time the workgroup streams neighbouring pages.
-    const int my_chunks = wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;
+    const int my_chunks = cw < nchunks ? (nchunks - cw + NW - 1) / NW : 0;
     for (int seg = 0; seg < my_chunks; seg += 32) {
         const int segn = min(32, my_chunks - seg);
-        const int tch = wave + (seg + (lane >> 1)) * NW;      // chunk of this lane's page
+        const int tch = cw + (seg + (lane >> 1)) * NW;        // chunk of this lane's page
         const int tb = 2 * tch + (lane & 1);
         const bool tok = lane < 2 * segn && tb < nblk;
         const int tbl = !tok ? -1 : (seg == 0 ? tbl0 : bt[blk0 + tb]);
         auto load = [&](Chunk<KV>& c, int k) __attribute__((always_inline)) {  // k: index in segment
             const int kk = min(k, segn - 1);
-            const int ch = wave + (seg + kk) * NW;
+            const int ch = cw + (seg + kk) * NW;
             Dk::load(c, p, kvh, __builtin_amdgcn_readlane(tbl, 2 * kk),
                      __builtin_amdgcn_readlane(tbl, 2 * kk + 1), 2 * ch + 1 < nblk, lane);
         };
@@ -455,10 +466,10 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
         load(ca, 0);
         for (int k = 0; k < segn; k += 2) {
             load(cb, k + 1);
-            process_chunk<KV, NW>(st, ca, qop, cscale, tok0 + 32 * (wave + (seg + k) * NW), tok1, g);
+            process_chunk<KV, NW>(st, ca, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, g);
             if (k + 1 >= segn) break;
             load(ca, k + 2);
-            process_chunk<KV, NW>(st, cb, qop, cscale, tok0 + 32 * (wave + (seg + k + 1) * NW), tok1, g);
+            process_chunk<KV, NW>(st, cb, qop, cscale, tok0 + 32 * (cw + (seg + k + 1) * NW), tok1, g);
         }
     }
 
