@@ -270,6 +270,10 @@ __device__ void merge_group(const DecodeParams& p, int64_t row0, int G, int npar
                 lk[u] = lp[k + u * KS];
                 ov[u] = op[(int64_t)(k + u * KS) * (D / 4)];
             }
+            // all 16 loads in one round trip: without this the compiler sinks
+            // the partial loads into the branch below, behind the LSE loads
+#pragma unroll
+            for (int u = 0; u < 8; ++u) pin(ov[u]);
             float mb = m;
 #pragma unroll
             for (int u = 0; u < 8; ++u) mb = fmaxf(mb, lk[u]);

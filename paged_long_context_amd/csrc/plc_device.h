@@ -172,4 +172,11 @@ __device__ __forceinline__ T load_nt(const T* p) {
     return __builtin_nontemporal_load(p);
 }
 
+// Materialises v in registers at this point.  Arithmetic that produces v
+// cannot be sunk past it, and loads that produce v are issued before it (the
+// compiler may otherwise sink work into a later branch or past a barrier,
+// which orders memory only).
+template <typename T>
+__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
+
 }  // namespace plc

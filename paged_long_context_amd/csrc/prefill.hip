@@ -193,12 +193,6 @@ __device__ __forceinline__ void stage_store_v(const Stage<KV>& st, f16* lv, floa
         }
 }
 
-// Materialises v in registers at this point: arithmetic that produces v
-// cannot be sunk past it (a workgroup barrier orders memory only, so the
-// compiler may otherwise move the softmax into the next MFMA phase).
-template <typename T>
-__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
-
 // Phase barrier: every wave of the workgroup; the scheduler moves nothing
 // across it, so the MFMA and VALU phases stay as written.
 __device__ __forceinline__ void phase_barrier() {
