@@ -111,11 +111,12 @@ struct Decode {
     // explicit vmcnt counts instead (unknown vector loads can only make the
     // compiler's own counts wait longer, never shorter).
     // M0 (the LDS base it reads at issue) is saved and restored around it.
+    // The loads are non-temporal: a step reads every page once.
     __device__ __forceinline__ static void dma16(const uint8_t* src, uint8_t* dst) {
         const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
         uint32_t saved;
         asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                     "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                     "global_load_lds_dwordx4 %2, off nt\n\ts_mov_b32 m0, %0"
                      : "=&s"(saved) : "s"(base), "v"(src) : "memory");
     }
     __device__ __forceinline__ static int swap02(int x) { return (x & ~5) | ((x & 1) << 2) | ((x >> 2) & 1); }
