@@ -3,9 +3,10 @@
 // One workgroup per (partition, KV head, sequence).  The partition's 16-token
 // pages are walked two at a time (a 32-token chunk) by the workgroup's waves.
 // Per chunk a wave:
-//   - reads the two page ids once and issues 16-byte K loads and 8-byte V
-//     loads straight into registers (the page-id reuse and wide loads that the
-//     1Cat-vLLM README's "128-bit Loads" section credits for its decode gain);
+//   - reads the two page ids once and moves the pages into its LDS buffer by
+//     DMA in whole kilobytes, 16 bytes per lane (the page-id reuse and wide
+//     loads that the 1Cat-vLLM README's "128-bit Loads" section credits for
+//     its decode gain), FP16 V going to registers instead;
 //   - converts K codes to fp16 and forms S^T = K * Q^T with the G query heads of
 //     the KV head as the 16-wide MFMA N dimension (GQA packing, Layer 2 "GQA
 //     Multi-Head Packing"); every lane therefore owns one query head;
@@ -47,64 +48,36 @@ template <int KV, int NW>
 struct Decode {
     static constexpr int EB = ElemBytes<KV>::value;
 
-    __device__ __forceinline__ static void load(Chunk<KV>& c, const DecodeParams& p, int kvh, int pb0, int pb1,
-                                bool has1, int lane) {
-        const int g = lane >> 4, i = lane & 15;
-        const int nb = p.kv.num_blocks;
-        c.valid_blk = ((pb0 >= 0 && pb0 < nb) ? 1 : 0) | ((has1 && pb1 >= 0 && pb1 < nb) ? 2 : 0);
-        const int pbs[2] = {(c.valid_blk & 1) ? pb0 : 0, (c.valid_blk & 2) ? pb1 : 0};
-        const int Hkv = p.kv.num_kv_heads;
-        const uint8_t* kc = static_cast<const uint8_t*>(p.kv.k);
-        const uint8_t* vc = static_cast<const uint8_t*>(p.kv.v);
-#pragma unroll
-        for (int pg = 0; pg < 2; ++pg) {
-            const int64_t base = ((int64_t)pbs[pg] * Hkv + kvh) * (BS * D * EB);
-            const uint8_t* kr = kc + base + i * (D * EB);
-            if constexpr (KV == KV_FP16) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int sub = 0; sub < 2; ++sub)
-                        c.kh[pg][2 * h + sub] =
-                            *reinterpret_cast<const f16x8*>(kr + (64 * h + 16 * g + 8 * sub) * 2);
-            } else {
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    c.k[pg][h] = *reinterpret_cast<const u32x4*>(kr + 64 * h + 16 * g);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int pg = e >> 2;
-            const int slot = 4 * g + (e & 3);
-            const int64_t base = ((int64_t)pbs[pg] * Hkv + kvh) * (BS * D * EB);
-            const uint8_t* vr = vc + base + slot * (D * EB) + 8 * i * EB;
-            if constexpr (KV == KV_FP16)
-                c.v16[e] = *reinterpret_cast<const u32x4*>(vr);
-            else
-                c.v8[e] = *reinterpret_cast<const u32x2*>(vr);
-        }
-        if constexpr (KV == KV_INT8) {
-#pragma unroll
-            for (int pg = 0; pg < 2; ++pg) {
-                const int64_t srow = ((int64_t)pbs[pg] * Hkv + kvh) * BS + 4 * g;
-                c.ks[pg] = *reinterpret_cast<const f32x4*>(p.kv.k_scale + srow);
-                c.vs[pg] = *reinterpret_cast<const f32x4*>(p.kv.v_scale + srow);
-            }
-        }
-    }
-
-    // ---- 8-bit codes: a chunk's four pages-halves of K and V reach a per-wave
-    // LDS buffer by DMA (global_load_lds, 16 bytes per lane, every instruction
-    // one contiguous kilobyte), and the operands are read from there.  LDS row
-    // slot s of a page holds token row swap02(s) (bits 0 and 2 swapped) with
-    // its 16-byte chunk c at chunk slot c ^ kap(s), kap(s) = (s & 7) ^ (s >> 3
-    // & 1): the DMA writes whole rows, and the K operand reads (16 rows, one
-    // chunk) and V row reads (two rows 4 apart) hit every bank at most once.
+    // ---- Pages reach a per-wave LDS buffer (two 8 KiB chunk buffers per wave,
+    // ping-pong) by DMA: global_load_lds, 16 bytes per lane, every instruction
+    // one contiguous kilobyte; the operands are then read from LDS.
+    //  8-bit codes: K pages at 0 and 2048, V pages at 4096 and 6144.  LDS row
+    //   slot s of a page holds token row swap02(s) (bits 0 and 2 swapped) with
+    //   its 16-byte chunk c at chunk slot c ^ kap(s), kap(s) = (s & 7) ^ (s >> 3
+    //   & 1): the K operand reads (16 rows, one chunk) and V row reads (two rows
+    //   4 apart) hit every bank at most once.
+    //  FP16: K pages at 0 and 4096 (256-byte rows), chunk c of row s at slot
+    //   c ^ s; V (whole 256-byte rows per 16-lane group already) stays in
+    //   registers.
     struct Meta {
         f32x4 ks[2], vs[2];          // INT8 per-token scales, as in Chunk
+        u32x4 v16[(KV == KV_FP16) ? 8 : 1];   // FP16 V rows, as in Chunk
         int valid_blk;
     };
+    __device__ __forceinline__ static int swap02(int x) { return (x & ~5) | ((x & 1) << 2) | ((x >> 2) & 1); }
+    __device__ __forceinline__ static int kap(int s) { return (s & 7) ^ ((s >> 3) & 1); }
+    // DMA instructions per page (8-bit: K and V, 2 each; FP16: K, 4)
+    static constexpr int kDmaPerPage = (KV == KV_FP16) ? 4 : 2;
+    // lane l's source offset within a page for DMA instruction q
+    __device__ __forceinline__ static int dma_src(int lane, int q) {
+        if constexpr (KV == KV_FP16) {
+            const int s = 4 * q + (lane >> 4);
+            return s * (D * 2) + 16 * ((lane & 15) ^ s);
+        } else {
+            const int s = 8 * q + (lane >> 3);
+            return swap02(s) * D + 16 * ((lane & 7) ^ kap(s));
+        }
+    }
     // One global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS
     // dst + 16 l (dst wave-uniform).  Written as asm so that the compiler does
     // not treat every later LDS read as waiting on it: the loop waits with
@@ -119,30 +92,36 @@ struct Decode {
                      "global_load_lds_dwordx4 %2, off nt\n\ts_mov_b32 m0, %0"
                      : "=&s"(saved) : "s"(base), "v"(src) : "memory");
     }
-    __device__ __forceinline__ static int swap02(int x) { return (x & ~5) | ((x & 1) << 2) | ((x >> 2) & 1); }
-    __device__ __forceinline__ static int kap(int s) { return (s & 7) ^ ((s >> 3) & 1); }
-    // lane l's source offset within a page for DMA instruction q (LDS slots 8q..8q+7)
-    __device__ __forceinline__ static int dma_src(int lane, int q) {
-        const int s = 8 * q + (lane >> 3);
-        return swap02(s) * D + 16 * ((lane & 7) ^ kap(s));
-    }
-    // buffer: 8192 bytes, K pages at 0 and 2048, V pages at 4096 and 6144
     __device__ __forceinline__ static void issue(Meta& m, uint8_t* lbuf, const DecodeParams& p, int kvh, int pb0,
-                                                 int pb1, bool has1, int lane, const int src[2]) {
-        const int g = lane >> 4;
+                                                 int pb1, bool has1, int lane, const int src[kDmaPerPage]) {
+        const int g = lane >> 4, i = lane & 15;
         const int nb = p.kv.num_blocks;
         m.valid_blk = ((pb0 >= 0 && pb0 < nb) ? 1 : 0) | ((has1 && pb1 >= 0 && pb1 < nb) ? 2 : 0);
         const int pbs[2] = {(m.valid_blk & 1) ? pb0 : 0, (m.valid_blk & 2) ? pb1 : 0};
         const int Hkv = p.kv.num_kv_heads;
 #pragma unroll
         for (int pg = 0; pg < 2; ++pg) {
-            const int64_t base = ((int64_t)pbs[pg] * Hkv + kvh) * (BS * D);
+            const int64_t base = ((int64_t)pbs[pg] * Hkv + kvh) * (BS * D * EB);
             const uint8_t* kp = static_cast<const uint8_t*>(p.kv.k) + base;
             const uint8_t* vp = static_cast<const uint8_t*>(p.kv.v) + base;
+            if constexpr (KV == KV_FP16) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                dma16(kp + src[q], lbuf + 2048 * pg + 1024 * q);
-                dma16(vp + src[q], lbuf + 4096 + 2048 * pg + 1024 * q);
+                for (int q = 0; q < 4; ++q) dma16(kp + src[q], lbuf + 4096 * pg + 1024 * q);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    dma16(kp + src[q], lbuf + 2048 * pg + 1024 * q);
+                    dma16(vp + src[q], lbuf + 4096 + 2048 * pg + 1024 * q);
+                }
+            }
+        }
+        if constexpr (KV == KV_FP16) {
+            // V: token 4g + e%4 of page e/4, d = 8i..8i+7, one 16-byte load each
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t base = ((int64_t)pbs[e >> 2] * Hkv + kvh) * (BS * D * EB);
+                m.v16[e] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(p.kv.v) + base +
+                                                           (4 * g + (e & 3)) * (D * EB) + 16 * i);
             }
         }
         if constexpr (KV == KV_INT8) {
@@ -155,19 +134,31 @@ struct Decode {
         }
     }
     // vector memory operations issue() puts in flight
-    static constexpr int kIssueOps = (KV == KV_INT8) ? 12 : 8;
-    // The chunk's operands from LDS: lane (i, g) reads token row i's chunks
-    // 4h + g of K and the 8 bytes d = 8i.. of V tokens 16(e>>2) + 4g + (e&3).
-    __device__ __forceinline__ static void read(Chunk<KV>& c, const Meta& m, const uint8_t* lbuf, const int kofs[2],
+    static constexpr int kIssueOps = (KV == KV_FP16) ? 16 : (KV == KV_INT8) ? 12 : 8;
+    // The chunk's operands from LDS.  8-bit: lane (i, g) reads token row i's
+    // chunks 4h + g of K (kofs[h]) and the 8 bytes d = 8i.. of V tokens
+    // 16(e>>2) + 4g + (e&3) (vofs[e&3]).  FP16: token row i's chunks
+    // 8h + 2g + sub of K (kofs[2h + sub]).
+    __device__ __forceinline__ static void read(Chunk<KV>& c, const Meta& m, const uint8_t* lbuf, const int kofs[4],
                                                 const int vofs[4]) {
+        if constexpr (KV == KV_FP16) {
 #pragma unroll
-        for (int pg = 0; pg < 2; ++pg)
+            for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                c.k[pg][h] = *reinterpret_cast<const u32x4*>(lbuf + 2048 * pg + kofs[h]);
+                for (int kc = 0; kc < 4; ++kc)
+                    c.kh[pg][kc] = *reinterpret_cast<const f16x8*>(lbuf + 4096 * pg + kofs[kc]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            c.v8[e] = *reinterpret_cast<const u32x2*>(lbuf + 4096 + 2048 * (e >> 2) + vofs[e & 3]);
+            for (int e = 0; e < 8; ++e) c.v16[e] = m.v16[e];
+        } else {
+#pragma unroll
+            for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    c.k[pg][h] = *reinterpret_cast<const u32x4*>(lbuf + 2048 * pg + kofs[h]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                c.v8[e] = *reinterpret_cast<const u32x2*>(lbuf + 4096 + 2048 * (e >> 2) + vofs[e & 3]);
+        }
         c.ks[0] = m.ks[0]; c.ks[1] = m.ks[1];
         c.vs[0] = m.vs[0]; c.vs[1] = m.vs[1];
         c.valid_blk = m.valid_blk;
@@ -410,13 +401,10 @@ __device__ void merge_group(const DecodeParams& p, int64_t row0, int G, int npar
 template <int KV, int NW>
 __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     using Dk = Decode<KV, NW>;
-    // 8-bit codes stream through per-wave LDS buffers (two 8 KiB chunks per
-    // wave); the wave merge and the fused merge reuse that space afterwards.
-    // FP16 loads straight into registers and takes its merge space dynamically.
-    constexpr bool DMA = KV != KV_FP16;
-    __shared__ __attribute__((aligned(16))) uint8_t s_dma[DMA ? NW : 1][DMA ? 2 : 1][DMA ? 8192 : 16];
-    extern __shared__ float smem_dyn[];
-    float* smem = DMA ? reinterpret_cast<float*>(&s_dma[0][0][0]) : smem_dyn;
+    // Pages stream through per-wave LDS buffers (two 8 KiB chunks per wave);
+    // the wave merge and the fused merge reuse that space afterwards.
+    __shared__ __attribute__((aligned(16))) uint8_t s_dma[NW][2][8192];
+    float* smem = reinterpret_cast<float*>(&s_dma[0][0][0]);
     __shared__ int s_last;
     const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -529,13 +517,18 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     for (int c = 0; c < 8; ++c) st.acc[c] = f32x4{0, 0, 0, 0};
 
     // per-lane LDS offsets of the DMA path (see Decode::issue / Decode::read)
-    int dsrc[2], kofs[2], vofs[4];
-    if constexpr (DMA) {
-        dsrc[0] = Dk::dma_src(lane, 0);
-        dsrc[1] = Dk::dma_src(lane, 1);
+    int dsrc[Dk::kDmaPerPage], kofs[4], vofs[4];
+#pragma unroll
+    for (int q = 0; q < Dk::kDmaPerPage; ++q) dsrc[q] = Dk::dma_src(lane, q);
+    if constexpr (KV == KV_FP16) {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) kofs[kc] = i * (2 * D) + 16 * ((8 * (kc >> 1) + 2 * g + (kc & 1)) ^ i);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) vofs[x] = 0;
+    } else {
         const int sk = Dk::swap02(i);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) kofs[h] = sk * D + 16 * ((4 * h + g) ^ Dk::kap(sk));
+        for (int h = 0; h < 4; ++h) kofs[h] = sk * D + 16 * ((4 * (h & 1) + g) ^ Dk::kap(sk));
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int sv = Dk::swap02(4 * g + x);
@@ -558,59 +551,39 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
         const int tb = 2 * tch + (lane & 1);
         const bool tok = lane < 2 * segn && tb < nblk;
         const int tbl = !tok ? -1 : (seg == 0 ? tbl0 : bt[blk0 + tb]);
-        auto load = [&](Chunk<KV>& c, int k) __attribute__((always_inline)) {  // k: index in segment
-            const int kk = min(k, segn - 1);
-            const int ch = cw + (seg + kk) * NW;
-            Dk::load(c, p, kvh, __builtin_amdgcn_readlane(tbl, 2 * kk),
-                     __builtin_amdgcn_readlane(tbl, 2 * kk + 1), 2 * ch + 1 < nblk, lane);
+        // two LDS buffers in ping-pong: the next chunk's DMA is in flight
+        // while the current one is computed; before reading a chunk the
+        // wave waits until only the next chunk's operations are pending
+        // (none after the segment's last chunk, so no DMA outlives it)
+        auto issue = [&](typename Dk::Meta& m, int b, int k) __attribute__((always_inline)) {
+            const int ch = cw + (seg + k) * NW;
+            Dk::issue(m, &s_dma[wave][b][0], p, kvh, __builtin_amdgcn_readlane(tbl, 2 * k),
+                      __builtin_amdgcn_readlane(tbl, 2 * k + 1), 2 * ch + 1 < nblk, lane, dsrc);
         };
-        if constexpr (DMA) {
-            // two LDS buffers in ping-pong: the next chunk's DMA is in flight
-            // while the current one is computed; before reading a chunk the
-            // wave waits until only the next chunk's operations are pending
-            // (none after the segment's last chunk, so no DMA outlives it)
-            auto issue = [&](typename Dk::Meta& m, int b, int k) __attribute__((always_inline)) {
-                const int ch = cw + (seg + k) * NW;
-                Dk::issue(m, &s_dma[wave][b][0], p, kvh, __builtin_amdgcn_readlane(tbl, 2 * k),
-                          __builtin_amdgcn_readlane(tbl, 2 * k + 1), 2 * ch + 1 < nblk, lane, dsrc);
-            };
-            typename Dk::Meta ma, mb;
-            Chunk<KV> c;
-            issue(ma, 0, 0);
-            for (int k = 0; k < segn; k += 2) {
-                if (k + 1 < segn) {
-                    issue(mb, 1, k + 1);
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Dk::kIssueOps) : "memory");
-                } else {
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                }
-                Dk::read(c, ma, &s_dma[wave][0][0], kofs, vofs);
-                process_chunk<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, g);
-                if (k + 1 >= segn) break;
-                if (k + 2 < segn) {
-                    issue(ma, 0, k + 2);
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Dk::kIssueOps) : "memory");
-                } else {
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                }
-                Dk::read(c, mb, &s_dma[wave][1][0], kofs, vofs);
-                process_chunk<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k + 1) * NW), tok1, g);
+        typename Dk::Meta ma, mb;
+        Chunk<KV> c;
+        issue(ma, 0, 0);
+        for (int k = 0; k < segn; k += 2) {
+            if (k + 1 < segn) {
+                issue(mb, 1, k + 1);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Dk::kIssueOps) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
-        } else {
-            // two register buffers in ping-pong: the next chunk's loads are in
-            // flight while the current one is computed
-            Chunk<KV> ca, cb;
-            load(ca, 0);
-            for (int k = 0; k < segn; k += 2) {
-                load(cb, k + 1);
-                process_chunk<KV, NW>(st, ca, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, g);
-                if (k + 1 >= segn) break;
-                load(ca, k + 2);
-                process_chunk<KV, NW>(st, cb, qop, cscale, tok0 + 32 * (cw + (seg + k + 1) * NW), tok1, g);
+            Dk::read(c, ma, &s_dma[wave][0][0], kofs, vofs);
+            process_chunk<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, g);
+            if (k + 1 >= segn) break;
+            if (k + 2 < segn) {
+                issue(ma, 0, k + 2);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Dk::kIssueOps) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
+            Dk::read(c, mb, &s_dma[wave][1][0], kofs, vofs);
+            process_chunk<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k + 1) * NW), tok1, g);
         }
     }
-    if constexpr (DMA) __syncthreads();                // the merge below reuses the DMA buffers
+    __syncthreads();                                   // the merge below reuses the DMA buffers
 
     // ---- merge the waves of the workgroup (fixed order) ----
     float l_run = st.l;
@@ -688,11 +661,10 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
 template <int KV, int NW>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
     const int G = p.num_q_heads / p.kv.num_kv_heads;
-    // wave-merge buffers (the fused merge reuses the same space); the 8-bit
-    // kernels carve them from their static DMA buffers instead
-    const size_t lds = KV != KV_FP16 ? 0
-                                     : sizeof(float) * max((size_t)NW * 32 + (size_t)NW * G * (D + 4),
-                                                           (size_t)2 * NW * (32 * 4 + 2));
+    // the wave-merge and fused-merge buffers live in the kernel's static DMA
+    // buffers (NW * 16 KiB; at most NW * (32 + 16 * 132) floats are needed)
+    static_assert(NW * 16384 >= 4 * NW * (32 + 16 * (D + 4)), "merge space");
+    const size_t lds = 0;
     dim3 grid(p.nparts, p.kv.num_kv_heads, p.num_seqs);
     hipLaunchKernelGGL((paged_decode_kernel<KV, NW>), grid, dim3(64 * NW), lds, s, p);
     return hipGetLastError();
