@@ -81,9 +81,13 @@ struct StageAddr {
     int32_t ks_row, vs_row;                          // scale rows within a page
 };
 
+// The table entry of key's page, read unconditionally at an index clamped to
+// the visible keys and used raw: stage_load checks it against num_blocks and
+// zeroes keys past kend, so nothing consumes the load before the tile is
+// staged two phases later (a select on it here would wait for the load in
+// the very next phase).
 __device__ __forceinline__ int page_of(const int32_t* bt, int key, int kend) {
-    const int pg = bt[(uint32_t)min(key, kend - 1) / BS];   // unconditional read
-    return key < kend ? pg : -1;
+    return bt[(uint32_t)min(key, kend - 1) / BS];
 }
 
 template <int KV>
