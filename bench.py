@@ -20,7 +20,7 @@ FP16 / E4M3 / INT8, and the CPU oracle timed on the host cores.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu]
 
 Profiling aids (no bench line): --prefill-only runs and times just the chunked
-prefill; --copy-calibration runs a plain 256 MiB device copy five times, the
+prefill; --verify-only just the verification decode; --copy-calibration runs a plain 256 MiB device copy five times, the
 known-size kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters.
 """
 import argparse
@@ -60,6 +60,8 @@ def parse():
                     help="time only the headline step (no per-part graphs), e.g. under a profiler")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill workload (for profiling)")
+    ap.add_argument("--verify-only", action="store_true",
+                    help="run only the verification-decode workload (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 256 MiB device copy 5 times and exit (counter calibration)")
     return ap.parse_args()
@@ -97,6 +99,68 @@ def append_bytes(w, dtype):
         b += T * s.num_kv_heads * 2 * 4
     b += (3 * s.num_seqs + 1) * 4                                         # cu, start, table
     return b
+
+
+def verify_bytes(w, dtype):
+    """Algorithmic HBM bytes of one verification call: decode_bytes's keys,
+    values, scales and table entries, every query token's row read, its
+    output row and LSE written, and cu_q_lens."""
+    s = w.spec
+    T = int(w.cu_q_lens[-1])
+    b = decode_bytes(w, dtype, with_outputs=False) - s.num_seqs * s.num_q_heads * s.head_dim * 2
+    b += T * s.num_q_heads * s.head_dim * 2 + T * s.num_q_heads * (s.head_dim + 1) * 4
+    return b + (s.num_seqs + 1) * 4
+
+
+def bench_verify(plc, synthetic, specs, K, widths=(4, 16)):
+    """Verification decode at the decode batch's shape (8 x 32768, E4M3,
+    partitions of 2048), 8 rotated cache copies, for a few draft widths."""
+    import dataclasses
+    res = {}
+    for n in widths:
+        sp = dataclasses.replace(specs["verify"], q_lens=[n] * len(specs["verify"].context_lens))
+        log("generating verify n=%d" % n)
+        w = synthetic.generate(sp)
+        s = w.spec
+        caches, bt = build_cache(plc, w, "e4m3", 8)
+        kn, vn = w.new_kv()
+        kn, vn = to_dev(kn), to_dev(vn)
+        cu, start, ctx = to_dev(w.cu_q_lens), to_dev(w.start_pos), to_dev(w.context_lens)
+        for c in caches:
+            plc.kv_append_quant(c, kn, vn, bt, cu, start)
+        q = to_dev(w.q)
+        T = int(w.cu_q_lens[-1])
+        maxc = int(w.context_lens.max())
+        P = s.partition_tokens
+        ws = torch.zeros(plc.verify_workspace_size(s.num_seqs, T, s.num_q_heads, s.num_kv_heads,
+                                                   s.head_dim, n, maxc, P),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty((T, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+        lse = torch.empty((T, s.num_q_heads), dtype=torch.float32, device="cuda")
+        sm = 1.0 / math.sqrt(s.head_dim)
+
+        def f(i):
+            plc.attn_verify_paged(q, caches[i % len(caches)], bt, cu, ctx, n, maxc, P, sm, out=out,
+                                  lse=lse, workspace=ws)
+        for i in range(3):
+            f(i)
+        _, ev = graph_time(f, max(5, min(50, K // 4)), reps=2)
+        vb = verify_bytes(w, "e4m3")
+        L = w.context_lens.astype(np.int64)
+        visible = int(sum(n * (int(l) - n) + n * (n + 1) // 2 for l in L))
+        fl = 4 * s.head_dim * s.num_q_heads * visible
+        res["n%d" % n] = {
+            "drafted_tokens": n, "gbs": round(vb / ev / 1e9, 1), "unit": "GB/s",
+            "us_per_call": round(ev * 1e6, 2), "bytes": vb,
+            "frac_of_hbm_peak": round(vb / ev / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(fl / ev / 1e12, 2),
+        }
+        log("verify n=%d: %.2f us = %.0f GB/s (%.1f%% of HBM), %.1f TFLOP/s"
+            % (n, ev * 1e6, vb / ev / 1e9, 100 * vb / ev / 1e9 / HBM_PEAK_GBS, fl / ev / 1e12))
+        del caches, ws, out, lse, q
+        torch.cuda.empty_cache()
+    res["workload"] = specs["verify"].description + "; widths as listed"
+    return res
 
 
 def prefill_flops(w):
@@ -346,6 +410,9 @@ def main():
     if args.prefill_only:
         print(json.dumps({"c3_prefill": bench_prefill(plc, synthetic, specs, K)}), flush=True)
         return
+    if args.verify_only:
+        print(json.dumps({"verify_e4m3": bench_verify(plc, synthetic, specs, K)}), flush=True)
+        return
 
     # ---------------- headline: C2 decode step ----------------
     log("generating c2 (8 x 32768, e4m3)")
@@ -435,6 +502,7 @@ def main():
                     % (name, dt, sw * 1e6, sb / sw / 1e9, ke * 1e6, kb / ke / 1e9))
                 del c
                 torch.cuda.empty_cache()
+        extra["verify_e4m3"] = bench_verify(plc, synthetic, specs, K)
         result["other_workloads"] = extra
 
     if not args.no_cpu:

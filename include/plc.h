@@ -191,6 +191,41 @@ int plc_attn_decode_append(const void* q, const void* k_new, const void* v_new,
                            void* stream);
 
 /*
+ * Verification decode (speculative decoding: the target model scores several
+ * drafted tokens per sequence in one step; ReVolta 0.1.2 release notes, the
+ * DFlash2 settings that verify 3, 4 or 7 drafts per request; 1Cat-vLLM README,
+ * installation check of the grouped-verify maximum query length).  Each
+ * sequence b has n_b = cu_q_lens[b+1] - cu_q_lens[b] query tokens, in
+ * [0, max_q_len], already appended as its last n_b positions; row j of b
+ * attends causally to keys 0 .. context_lens[b] - n_b + j (the chunked-prefill
+ * rule of plc_attn_prefill_paged), computed split-KV over partition_tokens
+ * and merged in the same launch as plc_attn_decode_paged does.  With n_b = 1
+ * for every b it computes what plc_attn_decode_paged computes.
+ *  q (device): fp16 [total_q_tokens][num_q_heads][head_dim], sequence b's
+ *      tokens at rows cu_q_lens[b] ..; out fp32 [total_q_tokens][num_q_heads]
+ *      [head_dim], lse fp32 [total_q_tokens][num_q_heads].
+ *  cu_q_lens (device): int32 [num_seqs + 1], nondecreasing, cu_q_lens[0] = 0,
+ *      cu_q_lens[num_seqs] = total_q_tokens (trusted, like context_lens).
+ *  max_q_len (host): bound on every n_b, 1 .. PLC_VERIFY_MAX_Q_LEN (larger
+ *      counts are a prefill: PLC_ERR_INVALID_ARG); n_b above it is clamped.
+ *  partition_tokens: as for plc_attn_decode_paged (0 = automatic).
+ *  workspace: plc_verify_workspace_size bytes, zero-filled before its first
+ *      use; the call leaves its counters zero again.
+ * A row whose causal range holds no key (n_b > context_lens[b]) gets out 0
+ * and lse -inf.  Calls that share a workspace must not overlap.
+ */
+#define PLC_VERIFY_MAX_Q_LEN 16
+size_t plc_verify_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
+                                 int32_t max_context_len, int32_t partition_tokens);
+int plc_attn_verify_paged(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
+                          const int32_t* block_tables, int32_t max_blocks, const int32_t* cu_q_lens,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t total_q_tokens,
+                          int32_t max_q_len, int32_t max_context_len, int32_t partition_tokens,
+                          float sm_scale, float* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * First half of plc_attn_decode_paged: per-partition normalized outputs and
  * LSEs into the workspace, laid out as plc_lse_merge reads them (o_parts at
  * offset 0, lse_parts at *lse_parts_offset bytes, nparts in *nparts).

@@ -76,6 +76,11 @@ _lib.plc_attn_decode_append.argtypes = [_P, _P, _P, _i32, _KV, _P, _i32, _P, _i3
 _lib.plc_attn_decode_partials.restype = ctypes.c_int
 _lib.plc_attn_decode_partials.argtypes = [_P, _i32, _KV, _P, _i32, _P, _i32, _i32, _i32, _f32, _P,
                                           _sz, ctypes.POINTER(_i32), ctypes.POINTER(_sz), _P]
+_lib.plc_verify_workspace_size.restype = _sz
+_lib.plc_verify_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
+_lib.plc_attn_verify_paged.restype = ctypes.c_int
+_lib.plc_attn_verify_paged.argtypes = [_P, _i32, _KV, _P, _i32, _P, _P, _i32, _i32, _i32, _i32, _i32,
+                                       _f32, _P, _P, _P, _sz, _P]
 _lib.plc_lse_merge.restype = ctypes.c_int
 _lib.plc_lse_merge.argtypes = [_P, _P, _i32, _i32, _i32, _P, _P, _P]
 _lib.plc_debug_e4m3_to_f16.restype = ctypes.c_int
@@ -316,6 +321,52 @@ def attn_decode_partials(q: torch.Tensor, cache: KVCache, block_tables: torch.Te
     o = workspace[: rows * n * D * 4].view(torch.float32).view(rows, n, D)
     l = workspace[off.value: off.value + rows * n * 4].view(torch.float32).view(rows, n)
     return o, l
+
+
+VERIFY_MAX_Q_LEN = 16
+
+
+def verify_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim, max_q_len,
+                          max_context_len, partition_tokens=0) -> int:
+    return int(_lib.plc_verify_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads,
+                                              head_dim, max_q_len, max_context_len,
+                                              partition_tokens))
+
+
+def attn_verify_paged(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor,
+                      cu_q_lens: torch.Tensor, context_lens: torch.Tensor, max_q_len: int,
+                      max_context_len: int, partition_tokens: int = 0,
+                      sm_scale: Optional[float] = None, out=None, lse=None, workspace=None,
+                      stream=None):
+    """Verification decode: a few query tokens per sequence (the last n_b
+    positions), causal among themselves, split-KV with the merge in the same
+    launch; q fp16 [T][Hq][D] -> (out fp32 [T][Hq][D], lse fp32 [T][Hq])."""
+    T, Hq, D = q.shape
+    _need(q, "q", torch.float16)
+    _need(block_tables, "block_tables", torch.int32)
+    B = block_tables.shape[0]
+    _need(cu_q_lens, "cu_q_lens", torch.int32, (B + 1,))
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (T, Hq, D))
+    _need(lse, "lse", torch.float32, (T, Hq))
+    if workspace is None:
+        need = verify_workspace_size(B, T, Hq, cache.num_kv_heads, D, int(max_q_len),
+                                     int(max_context_len), int(partition_tokens))
+        # zero-filled: the merge's completion counters start at zero
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    _check(_lib.plc_attn_verify_paged(_ptr(q), Hq, cache.desc(), _ptr(block_tables),
+                                      block_tables.shape[1], _ptr(cu_q_lens), _ptr(context_lens), B, T,
+                                      int(max_q_len), int(max_context_len), int(partition_tokens),
+                                      float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)))
+    return out, lse
 
 
 def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out=None, lse=None, stream=None):

@@ -149,7 +149,15 @@ int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
     p.lse = nullptr;
     p.k_new = nullptr;
     p.v_new = nullptr;
+    p.cu_q_lens = nullptr;
+    p.max_q_len = 1;
+    p.ncg = 1;
     return PLC_OK;
+}
+
+// rows of one (sequence, KV head) in groups of 16, one workgroup column each
+int32_t verify_row_groups(int32_t num_q_heads, int32_t num_kv_heads, int32_t max_q_len) {
+    return (max_q_len * (num_q_heads / num_kv_heads) + 15) / 16;
 }
 
 }  // namespace
@@ -300,6 +308,85 @@ int plc_attn_decode_append(const void* q, const void* k_new, const void* v_new,
     p.v_new = v_new;
     return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)),
                       "decode-append launch");
+}
+
+size_t plc_verify_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
+                                 int32_t max_context_len, int32_t partition_tokens) {
+    if (num_seqs <= 0 || total_q_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_q_len < 1 ||
+        max_q_len > PLC_VERIFY_MAX_Q_LEN || max_context_len < 0)
+        return 0;
+    const int32_t ncg = verify_row_groups(num_q_heads, num_kv_heads, max_q_len);
+    const int32_t P = resolve_partition(num_seqs * ncg, num_kv_heads, max_context_len, partition_tokens);
+    const int64_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
+    const size_t rows = (size_t)total_q_tokens * num_q_heads;
+    // partial outputs and LSEs per query row, one completion counter per
+    // (sequence, KV head, row group)
+    return align_up(rows * nparts * head_dim * sizeof(float)) + align_up(rows * nparts * sizeof(float)) +
+           align_up((size_t)num_seqs * num_kv_heads * ncg * sizeof(int32_t));
+}
+
+int plc_attn_verify_paged(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
+                          const int32_t* block_tables, int32_t max_blocks, const int32_t* cu_q_lens,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t total_q_tokens,
+                          int32_t max_q_len, int32_t max_context_len, int32_t partition_tokens,
+                          float sm_scale, float* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    int rc;
+    if ((rc = check_cache(kv))) return rc;
+    if ((rc = check_heads(num_q_heads, kv))) return rc;
+    if ((rc = check_lengths(num_seqs, max_blocks, max_context_len, kv->block_size))) return rc;
+    if (total_q_tokens < 0)
+        return fail(PLC_ERR_INVALID_ARG, "total_q_tokens %d is negative", total_q_tokens);
+    if (max_q_len < 1 || max_q_len > PLC_VERIFY_MAX_Q_LEN)
+        return fail(PLC_ERR_INVALID_ARG, "max_q_len %d outside [1, %d]: longer chunks are prefill",
+                    max_q_len, PLC_VERIFY_MAX_Q_LEN);
+    if (max_q_len > max_context_len)
+        return fail(PLC_ERR_INVALID_ARG, "max_q_len %d exceeds max_context_len %d", max_q_len,
+                    max_context_len);
+    if (total_q_tokens == 0) return PLC_OK;
+    if (!q || !block_tables || !cu_q_lens || !context_lens || !out || !lse)
+        return fail(PLC_ERR_INVALID_ARG, "q / block_tables / cu_q_lens / context_lens / out / lse is NULL");
+    if (partition_tokens < 0 || partition_tokens % kv->block_size != 0)
+        return fail(PLC_ERR_INVALID_ARG, "partition_tokens %d must be 0 or a multiple of block_size %d",
+                    partition_tokens, kv->block_size);
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(PLC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
+    const int32_t ncg = verify_row_groups(num_q_heads, kv->num_kv_heads, max_q_len);
+    const int32_t P = resolve_partition(num_seqs * ncg, kv->num_kv_heads, max_context_len, partition_tokens);
+    const size_t need = plc_verify_workspace_size(num_seqs, total_q_tokens, num_q_heads, kv->num_kv_heads,
+                                                  kv->head_dim, max_q_len, max_context_len, P);
+    if (!workspace || workspace_bytes < need)
+        return fail(PLC_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                    workspace_bytes, workspace, need);
+    const int32_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
+    const size_t rows = (size_t)total_q_tokens * num_q_heads;
+    plc::DecodeParams p;
+    p.q = q;
+    p.kv = view(kv);
+    p.block_tables = block_tables;
+    p.max_blocks = max_blocks;
+    p.context_lens = context_lens;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.max_context_len = max_context_len;
+    p.partition_tokens = P;
+    p.nparts = nparts;
+    p.qk_scale_log2 = sm_scale * 1.4426950408889634f;
+    const size_t o_bytes = align_up(rows * nparts * kv->head_dim * sizeof(float));
+    const size_t l_bytes = align_up(rows * nparts * sizeof(float));
+    p.o_parts = static_cast<float*>(workspace);
+    p.lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + o_bytes + l_bytes);
+    p.out = out;
+    p.lse = lse;
+    p.k_new = nullptr;
+    p.v_new = nullptr;
+    p.cu_q_lens = cu_q_lens;
+    p.max_q_len = max_q_len;
+    p.ncg = ncg;
+    return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)), "verify launch");
 }
 
 int plc_lse_merge(const float* o_parts, const float* lse_parts, int32_t rows, int32_t nparts,

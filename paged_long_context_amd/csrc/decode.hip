@@ -236,20 +236,33 @@ struct WaveState {
     f32x4 acc[8];                  // O^T[d = 32g + 8r + c][head i] in acc[c][r]
 };
 
-template <int KV, int NW>
-__device__ __forceinline__ void process_chunk(WaveState& st, Chunk<KV>& cur, const f16x8 qop[4],
-                                              float cscale, int ctok, int tok1, int g) {
-    using Dk = Decode<KV, NW>;
-    // validity of the lane's eight tokens t(g, e)
-    bool ok[8];
+// lim1: the lane's query row scores keys below lim1 = min(tok1, its causal
+// limit) (tok1 itself for a one-token decode).  V validity (inside the
+// partition, on a valid page) is a property of the token, shared by every
+// row, and is only needed for a partial chunk; the causal limit masks scores.
+template <int KV>
+__device__ __forceinline__ void token_ok(bool v[8], int ctok, int lim, int valid_blk, int g) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int pg = e >> 2;
-        ok[e] = (ctok + 16 * pg + 4 * g + (e & 3) < tok1) && ((cur.valid_blk >> pg) & 1);
+        v[e] = (ctok + 16 * pg + 4 * g + (e & 3) < lim) && ((valid_blk >> pg) & 1);
     }
+}
+
+template <int KV, int NW>
+__device__ __forceinline__ void process_chunk(WaveState& st, Chunk<KV>& cur, const f16x8 qop[4],
+                                              float cscale, int ctok, int tok1, int lim1, int g) {
+    using Dk = Decode<KV, NW>;
+    // scored tokens of the lane's eight t(g, e)
+    bool ok[8];
+    token_ok<KV>(ok, ctok, lim1, cur.valid_blk, g);
     const bool partial = (ctok + 32 > tok1) || (cur.valid_blk != 3);
     if constexpr (KV != KV_FP16)
-        if (partial) Dk::mask_v(cur, ok);
+        if (partial) {
+            bool vok[8];
+            token_ok<KV>(vok, ctok, tok1, cur.valid_blk, g);
+            Dk::mask_v(cur, vok);
+        }
 
     // S^T = K Q^T per page: lane holds tokens 4g + r of page pg, head i.
     float x[8];
@@ -298,23 +311,37 @@ __device__ __forceinline__ void process_chunk(WaveState& st, Chunk<KV>& cur, con
     Dk::v_operands(cur, vt);
     if constexpr (KV == KV_FP16)
         if (partial) {
+            bool vok[8];
+            token_ok<KV>(vok, ctok, tok1, cur.valid_blk, g);
 #pragma unroll
             for (int c = 0; c < 8; ++c)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vt[c][e] = ok[e] ? vt[c][e] : (f16)0.0f;
+                for (int e = 0; e < 8; ++e) vt[c][e] = vok[e] ? vt[c][e] : (f16)0.0f;
         }
 #pragma unroll
     for (int c = 0; c < 8; ++c) st.acc[c] = mfma16(vt[c], pop, st.acc[c]);
 }
 
-// Merge the partitions of one (sequence, KV head) group; run by the workgroup
-// that finished last.  One pass over the partials, every thread holding
+// Query rows of one workgroup column: column c is row r = cg16 + c of its
+// (sequence, KV head) group, i.e. query token qa + r / G (position-major) and
+// head kvh * G + r % G.
+struct RowMap {
+    int64_t base;                   // row of the group's first query token's first head
+    int Hq, cg16, gshift;           // G = 1 << gshift (G is a power of two)
+    __device__ __forceinline__ int64_t row(int c) const {
+        const int r = cg16 + c;
+        return base + ((r >> gshift) * Hq + (r & ((1 << gshift) - 1)));
+    }
+};
+
+// Merge the partitions of one (sequence, KV head, row group); run by the
+// workgroup that finished last.  One pass over the partials, every thread holding
 // several 16-byte loads in flight: thread (sub, d4) owns columns 4*d4..+3 of
 // row j for the parts k = ks, ks + KS, ... of its subset and keeps a running
 // maximum; the subsets are then combined in a fixed order through LDS.
 // lds must hold 2 * NW * (32 * 4 + 2) floats.
 template <int NW>
-__device__ void merge_group(const DecodeParams& p, int64_t row0, int G, int nparts_b, int tid,
+__device__ void merge_group(const DecodeParams& p, const RowMap& rm, int G, int nparts_b, int tid,
                             float* lds) {
     constexpr int NSUB = 64 * NW / 32;                  // 32-lane groups (one row slice each)
     f32x4* s_acc = reinterpret_cast<f32x4*>(lds);       // [NSUB][32]
@@ -327,8 +354,9 @@ __device__ void merge_group(const DecodeParams& p, int64_t row0, int G, int npar
     const float NEG = -__builtin_inff();
     for (int j0 = 0; j0 < G; j0 += RP) {
         const int j = j0 + sub % RP, ks = sub / RP;
-        const float* lp = p.lse_parts + (row0 + j) * nparts;
-        const f32x4* op = reinterpret_cast<const f32x4*>(p.o_parts + (row0 + j) * nparts * D) + d4;
+        const int64_t row = rm.row(j < G ? j : 0);       // j >= G only in a spare pass slot
+        const float* lp = p.lse_parts + row * nparts;
+        const f32x4* op = reinterpret_cast<const f32x4*>(p.o_parts + row * nparts * D) + d4;
         f32x4 acc = f32x4{0, 0, 0, 0};
         float m = NEG, wsum = 0.0f;                      // running max (natural log units)
         int k = ks;
@@ -378,7 +406,7 @@ __device__ void merge_group(const DecodeParams& p, int64_t row0, int G, int npar
             s_w[sub] = wsum;
         }
         __syncthreads();
-        if (ks == 0) {
+        if (ks == 0 && j < G) {
             float M = NEG;
             for (int t = 0; t < KS; ++t) M = fmaxf(M, s_m[sub + t * RP]);
             f32x4 a = f32x4{0, 0, 0, 0};
@@ -391,14 +419,17 @@ __device__ void merge_group(const DecodeParams& p, int64_t row0, int G, int npar
                     ws += sc * s_w[o];
                 }
             const bool empty = !(ws > 0.0f);
-            reinterpret_cast<f32x4*>(p.out + (row0 + j) * D)[d4] = empty ? f32x4{0, 0, 0, 0} : a / ws;
-            if (d4 == 0) p.lse[row0 + j] = empty ? NEG : M + __builtin_logf(ws);
+            reinterpret_cast<f32x4*>(p.out + row * D)[d4] = empty ? f32x4{0, 0, 0, 0} : a / ws;
+            if (d4 == 0) p.lse[row] = empty ? NEG : M + __builtin_logf(ws);
         }
         __syncthreads();
     }
 }
 
-template <int KV, int NW>
+// MQ: several query tokens per sequence (p.cu_q_lens set); without it the
+// kernel is the one-token decode, with the row map and bounds it implies
+// folded at compile time.
+template <int KV, int NW, bool MQ>
 __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     using Dk = Decode<KV, NW>;
     // Pages stream through per-wave LDS buffers (two 8 KiB chunks per wave);
@@ -406,7 +437,9 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t s_dma[NW][2][8192];
     float* smem = reinterpret_cast<float*>(&s_dma[0][0][0]);
     __shared__ int s_last;
-    const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int part = blockIdx.x, b = blockIdx.z;
+    const int kvh = MQ ? (int)blockIdx.y / p.ncg : (int)blockIdx.y;
+    const int cg = MQ ? (int)blockIdx.y - kvh * p.ncg : 0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // Chunk c of the partition goes to the wave with cw = c mod NW, cw =
@@ -429,23 +462,34 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     const int L = max(0, min(p.context_lens[b], p.max_context_len));
     const int nparts_b = (L + P - 1) / P;
     const int tok0 = part * P;
-    const int64_t row0 = (int64_t)b * Hq + (int64_t)kvh * G;   // first query row of the group
     const int nparts = p.nparts;
+    // this workgroup's query rows: NC columns of the 16-wide N tile
+    int n = 1;
+    int64_t qa = b;                                              // the sequence's first query token
+    if constexpr (MQ) {
+        qa = p.cu_q_lens[b];
+        n = min(max(p.cu_q_lens[b + 1] - p.cu_q_lens[b], 0), p.max_q_len);
+    }
+    const RowMap rm{qa * Hq + kvh * G, Hq, 16 * cg, __builtin_ctz(G)};
+    const int NC = MQ ? min(16, n * G - 16 * cg) : G;
+    if (MQ && NC <= 0) return;                                   // no rows: no partials, no merge
 
     if (part >= nparts_b) {                                      // partition past the end
         if (p.counters) {
             // fused call: only a sequence with no key at all has work here
             if (part == 0)
-                for (int idx = tid; idx < G * D; idx += 64 * NW) {
-                    p.out[(row0 + idx / D) * D + idx % D] = 0.0f;
-                    if (idx % D == 0) p.lse[row0 + idx / D] = -__builtin_inff();
+                for (int idx = tid; idx < NC * D; idx += 64 * NW) {
+                    const int64_t row = rm.row(idx / D);
+                    p.out[row * D + idx % D] = 0.0f;
+                    if (idx % D == 0) p.lse[row] = -__builtin_inff();
                 }
             return;
         }
-        for (int idx = tid; idx < G * D; idx += 64 * NW) {
+        for (int idx = tid; idx < NC * D; idx += 64 * NW) {
             const int j = idx / D, d = idx % D;
-            p.o_parts[((row0 + j) * nparts + part) * D + d] = 0.0f;
-            if (d == 0) p.lse_parts[(row0 + j) * nparts + part] = -__builtin_inff();
+            const int64_t row = rm.row(j);
+            p.o_parts[(row * nparts + part) * D + d] = 0.0f;
+            if (d == 0) p.lse_parts[row * nparts + part] = -__builtin_inff();
         }
         return;
     }
@@ -490,13 +534,17 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     if constexpr (KV == KV_INT8)
         if (appends) __syncthreads();
 
-    // Q^T operand: lane (i, g) holds head i, d = 64*(kc/2) + 16g + 8*(kc%2) + [0, 8).
+    // Q^T operand: lane (i, g) holds row (column) i, d = 64*(kc/2) + 16g +
+    // 8*(kc%2) + [0, 8); its causal limit: position L - n + j sees keys below
+    // L - n + j + 1 (L for a one-token decode; nothing for a spare column).
     f16x8 qop[4];
+    const int lim = i < NC ? L - n + 1 + ((16 * cg + i) >> rm.gshift) : 0;
+    const int lim1 = MQ ? min(lim, tok1) : tok1;       // and inside the partition
     {
-        const f16* q = static_cast<const f16*>(p.q) + (row0 + i) * D;
+        const f16* q = static_cast<const f16*>(p.q) + rm.row(i < NC ? i : 0) * D;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-            if (i < G)
+            if (i < NC)
                 qop[kc] = *reinterpret_cast<const f16x8*>(q + 64 * (kc >> 1) + 16 * g + 8 * (kc & 1));
             else
                 qop[kc] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -571,7 +619,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             Dk::read(c, ma, &s_dma[wave][0][0], kofs, vofs);
-            process_chunk<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, g);
+            process_chunk<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, lim1, g);
             if (k + 1 >= segn) break;
             if (k + 2 < segn) {
                 issue(ma, 0, k + 2);
@@ -580,7 +628,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             Dk::read(c, mb, &s_dma[wave][1][0], kofs, vofs);
-            process_chunk<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k + 1) * NW), tok1, g);
+            process_chunk<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k + 1) * NW), tok1, lim1, g);
         }
     }
     __syncthreads();                                   // the merge below reuses the DMA buffers
@@ -592,13 +640,13 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     constexpr int AST = D + 4;                         // padded head stride (floats)
     float* s_m = smem;                                 // [NW][16]
     float* s_l = smem + NW * 16;                       // [NW][16]
-    float* s_acc = smem + NW * 32;                     // [NW][G][AST]
+    float* s_acc = smem + NW * 32;                     // [NW][NC][AST]
     if (g == 0) {
         s_m[wave * 16 + i] = st.m;
         s_l[wave * 16 + i] = l_run;
     }
-    if (i < G) {
-        float* dst = s_acc + ((int64_t)wave * G + i) * AST + 32 * g;
+    if (i < NC) {
+        float* dst = s_acc + ((int64_t)wave * NC + i) * AST + 32 * g;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             f32x4 lo = f32x4{st.acc[0][r], st.acc[1][r], st.acc[2][r], st.acc[3][r]};
@@ -608,7 +656,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += 64 * NW) {
+    for (int idx = tid; idx < NC * D; idx += 64 * NW) {
         const int j = idx / D, d = idx % D;
         float M = -__builtin_inff();
 #pragma unroll
@@ -619,14 +667,15 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
             for (int w = 0; w < NW; ++w) {
                 const float wt = fast_exp2(s_m[w * 16 + j] - M);
                 Lsum += s_l[w * 16 + j] * wt;
-                O += s_acc[((int64_t)w * G + j) * AST + d] * wt;
+                O += s_acc[((int64_t)w * NC + j) * AST + d] * wt;
             }
         }
         const bool empty = !(Lsum > 0.0f);
         const float ov = empty ? 0.0f : O * vscale / Lsum;
         const float lv = empty ? -__builtin_inff() : (M + __builtin_log2f(Lsum)) * kLn2;
-        float* od = p.o_parts + ((row0 + j) * nparts + part) * D + d;
-        float* ld = p.lse_parts + (row0 + j) * nparts + part;
+        const int64_t row = rm.row(j);
+        float* od = p.o_parts + (row * nparts + part) * D + d;
+        float* ld = p.lse_parts + row * nparts + part;
         if (p.counters) {
             // agent-coherent (write-through) stores: another workgroup, possibly
             // on another XCD, reads them without any L2 write-back here
@@ -646,7 +695,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
-        int* cnt = p.counters + (int64_t)b * p.kv.num_kv_heads + kvh;
+        int* cnt = p.counters + ((int64_t)b * p.kv.num_kv_heads + kvh) * p.ncg + cg;
         const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == nparts_b - 1);
         if (s_last)                                   // leave the counter zeroed for the next call
@@ -655,26 +704,33 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     __syncthreads();
     if (!s_last) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    merge_group<NW>(p, row0, G, nparts_b, tid, smem);
+    merge_group<NW>(p, rm, NC, nparts_b, tid, smem);
 }
 
-template <int KV, int NW>
-hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
-    const int G = p.num_q_heads / p.kv.num_kv_heads;
+template <int KV, int NW, bool MQ>
+hipError_t launch_mq(const DecodeParams& p, hipStream_t s) {
     // the wave-merge and fused-merge buffers live in the kernel's static DMA
     // buffers (NW * 16 KiB; at most NW * (32 + 16 * 132) floats are needed)
     static_assert(NW * 16384 >= 4 * NW * (32 + 16 * (D + 4)), "merge space");
     const size_t lds = 0;
-    dim3 grid(p.nparts, p.kv.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((paged_decode_kernel<KV, NW>), grid, dim3(64 * NW), lds, s, p);
+    dim3 grid(p.nparts, p.kv.num_kv_heads * p.ncg, p.num_seqs);
+    hipLaunchKernelGGL((paged_decode_kernel<KV, NW, MQ>), grid, dim3(64 * NW), lds, s, p);
     return hipGetLastError();
+}
+
+template <int KV, int NW>
+hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
+    if (p.cu_q_lens) return launch_mq<KV, NW, true>(p, s);
+    return launch_mq<KV, NW, false>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s) {
-    // LDS holds every wave's unnormalized output: keep it within 64 KiB
-    const bool wide = p.num_q_heads / p.kv.num_kv_heads > 8;
+    // 4 waves for a one-token decode of more than 8 heads per KV head, and
+    // for a verification with more than two 16-row groups (enough workgroups
+    // to fill the chip; measured faster from 8 drafted tokens at G = 8)
+    const bool wide = p.cu_q_lens ? p.ncg > 2 : p.num_q_heads / p.kv.num_kv_heads > 8;
     switch (p.kv.dtype) {
     case KV_FP16: return wide ? launch_t<KV_FP16, 4>(p, s) : launch_t<KV_FP16, 8>(p, s);
     case KV_E4M3: return wide ? launch_t<KV_E4M3, 4>(p, s) : launch_t<KV_E4M3, 8>(p, s);

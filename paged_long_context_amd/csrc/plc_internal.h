@@ -41,6 +41,15 @@ struct DecodeParams {
     // f16 [B][Hkv][D] each, or NULL
     const void* k_new;
     const void* v_new;
+    // Several query tokens per sequence (verification of drafted tokens), or
+    // NULL for one.  cu_q_lens int32 [B+1]: sequence b's n_b query tokens are
+    // its last n_b positions (n_b clamped to max_q_len); q, out, lse and the
+    // partials are indexed by row (cu_q_lens[b] + j) * Hq + head.  Without
+    // cu_q_lens, row b * Hq + head.  The rows of one (sequence, KV head) are
+    // split into ncg groups of 16 (position-major), one workgroup column each.
+    const int32_t* cu_q_lens;
+    int32_t max_q_len;
+    int32_t ncg;
 };
 
 hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s);

@@ -219,7 +219,8 @@ def c5_lengths(seed: int, n: int = 32, lo: int = 1024, hi: int = 131072) -> List
 
 
 def named_specs() -> Dict[str, Spec]:
-    """The five operator workloads (one GPU's share of heads)."""
+    """The five operator workloads (one GPU's share of heads), plus the
+    verification-decode workload at the decode batch's shape."""
     s = {}
     s["c1_prefill"] = Spec(
         name="c1_prefill", context_lens=[512], q_lens=[512], seed=BASE_SEED + 1,
@@ -243,6 +244,12 @@ def named_specs() -> Dict[str, Spec]:
         num_kv_heads=4, kv_dtypes=(KV_FP16, KV_E4M3, KV_INT8), seed=c5_seed,
         description="ragged decode: 32 sequences, log-uniform [1,024, 131,072], 32 q / 4 kv, "
                     "FP16 / E4M3 / INT8 KV")
+    # beyond the five: verification of drafted tokens at the decode batch's shape
+    s["verify"] = Spec(
+        name="verify", context_lens=[32768] * 8, q_lens=[4] * 8, partition_tokens=2048,
+        seed=BASE_SEED + 6,
+        description="verification decode: 8 x 32,768 context, 4 drafted tokens per sequence "
+                    "(causal among themselves), 8 q / 1 kv, E4M3, partitions of 2,048")
     return s
 
 

@@ -26,6 +26,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["plc_kv_append_quant", "plc_attn_prefill_paged", "plc_attn_decode_paged",
               "plc_lse_merge", "plc_attn_decode_partials", "plc_decode_workspace_size",
+              "plc_attn_verify_paged", "plc_verify_workspace_size",
               "plc_abi_version", "plc_last_error"]:
         assert n in names
 
@@ -131,3 +132,36 @@ def test_prefill_and_merge_and_append_validation(plc):
     assert L.plc_kv_append_quant(ctypes.byref(d), None, 0x1, 0x1, 4, 0x1, 0x1, 1, 5, None) == -1
     assert L.plc_kv_append_quant(ctypes.byref(d), None, None, None, 4, None, None, 1, 0, None) == 0
     assert L.plc_kv_append_quant(ctypes.byref(d), 0x1, 0x1, 0x1, 4, 0x1, 0x1, 0, 5, None) == -1
+
+
+def _verify(plc, desc, hq=8, max_q=4, max_ctx=64, total=8, part=0, ws_bytes=1 << 20, ws=0x2000,
+            q=0x3000):
+    return plc.lib().plc_attn_verify_paged(q, hq, ctypes.byref(desc), 0x4000, 4, 0x4800, 0x5000, 2,
+                                           total, max_q, max_ctx, part, 0.088, 0x6000, 0x7000, ws,
+                                           ws_bytes, None)
+
+
+def test_verify_validation(plc):
+    d = _desc(plc)
+    assert _verify(plc, d, max_q=0) == -1 and "max_q_len" in _err(plc)
+    assert _verify(plc, d, max_q=plc.VERIFY_MAX_Q_LEN + 1) == -1 and "prefill" in _err(plc)
+    assert _verify(plc, d, max_q=8, max_ctx=4) == -1                 # more queries than keys
+    assert _verify(plc, d, part=24) == -1 and "multiple" in _err(plc)
+    assert _verify(plc, d, q=None) == -1
+    assert _verify(plc, d, total=0, q=None) == 0                     # nothing to do
+    need = plc.verify_workspace_size(2, 8, 8, 1, 128, 4, 64, 0)
+    assert need > 0
+    assert _verify(plc, d, ws_bytes=need - 1) == -3 and "needed" in _err(plc)
+    assert _verify(plc, _desc(plc, dtype=1, scales=False)) == -1       # E4M3 needs its scales
+
+
+def test_verify_workspace_size_formula(plc):
+    # 8 sequences x 4 tokens x 8 heads = 256 rows, 16 partitions of 2048;
+    # 4 x 8 = 32 rows per (sequence, KV head) = 2 groups of 16 -> 16 counters
+    rows, nparts = 8 * 4 * 8, 16
+    want = ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
+    want += ((8 * 1 * 2 * 4 + 255) // 256) * 256
+    assert plc.verify_workspace_size(8, 32, 8, 1, 128, 4, 32768, 2048) == want
+    assert plc.verify_workspace_size(8, 32, 8, 1, 128, 0, 32768, 2048) == 0
+    assert plc.verify_workspace_size(8, 32, 8, 1, 128, 17, 32768, 2048) == 0
+
