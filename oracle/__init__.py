@@ -57,7 +57,7 @@ def lib():
         L.orc_kv_append.argtypes = [i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P]
         L.orc_attention.restype = ctypes.c_int
         L.orc_attention.argtypes = [P, i32, i32, P, P, P, P, i32, i32, i32, i32, P, i32, P, P, i32,
-                                    f64, P, i64, i64, i64, P, P, i32]
+                                    f64, P, i64, i64, i64, i64, P, P, i32]
         L.orc_lse_merge.restype = None
         L.orc_lse_merge.argtypes = [P, P, i64, i32, i32, P, P]
         _lib = L
@@ -149,8 +149,9 @@ class HostCache:
 # ---------------------------------------------------------------- attention
 
 def attention(q, num_q_heads, cache: HostCache, block_tables, cu_q_lens, context_lens,
-              sm_scale, rows=None, key_begin=0, key_end=2**62, nthreads=0):
-    """Attention for query rows (row id = token * Hq + head).
+              sm_scale, rows=None, key_begin=0, key_end=2**62, window=0, nthreads=0):
+    """Attention for query rows (row id = token * Hq + head).  window > 0
+    limits the query at position pos to keys pos - window + 1 .. pos.
 
     Returns (out [T][Hq][D] fp32, lse [T][Hq] fp32); rows not listed stay NaN.
     """
@@ -172,7 +173,7 @@ def attention(q, num_q_heads, cache: HostCache, block_tables, cu_q_lens, context
         _p(qb), num_q_heads, cache.code, _p(cache.k), _p(cache.v), _p(ks), _p(vs),
         cache.num_blocks, cache.block_size, cache.num_kv_heads, D, _p(bt), bt.shape[1],
         _p(cu), _p(cl), len(cl), float(sm_scale), _p(rows_a), n, int(key_begin), int(key_end),
-        _p(out), _p(lse), int(nthreads))
+        int(window), _p(out), _p(lse), int(nthreads))
     if rc != 0:
         raise ValueError("orc_attention failed (%d)" % rc)
     return out, lse

@@ -250,6 +250,7 @@ typedef struct {
     const int64_t* rows;
     int64_t n_rows;
     int64_t key_begin, key_end;
+    int64_t window;                 /* > 0: keys pos - window + 1 .. pos only */
     float* out;
     float* lse;
     /* decode tables built once per call from the format definitions */
@@ -296,6 +297,8 @@ static int orc_attention_row(const orc_attn_job* J, int64_t r, double* scores, d
     const int64_t L = J->context_lens[b];
     const int64_t pos = L - n + (t - J->cu_q_lens[b]);
     int64_t lo = J->key_begin > 0 ? J->key_begin : 0;
+    if (J->window > 0 && pos - J->window + 1 > lo)
+        lo = pos - J->window + 1;
     int64_t hi = pos + 1;
     if (J->key_end < hi)
         hi = J->key_end;
@@ -375,7 +378,12 @@ static void* orc_attention_worker(void* arg)
  * t indexes the packed new query tokens (q: f16 bits [T][Hq][D]).  out gets
  * fp32 [T][Hq][D] and lse fp32 [T][Hq] at the listed rows only.  Keys are the
  * row's causal range intersected with [key_begin, key_end) (absolute token
- * positions; pass 0 and INT64_MAX for the whole range).  Scales: E4M3 takes
+ * positions; pass 0 and INT64_MAX for the whole range) and, when window > 0,
+ * with the row's sliding window: the query at position pos sees only keys
+ * pos - window + 1 .. pos, the most recent window tokens including its own
+ * (1Cat-vLLM README, "DFlash2 Long-Context Decay": the draft attends over a
+ * sliding window; ReVolta 0.1.2 release notes: the DFlash2 drafter's
+ * 2048-token window).  Scales: E4M3 takes
  * [Hkv] per KV head, INT8 takes [num_blocks][Hkv][block_size] per token.
  * rows = NULL means every row 0 .. n_rows-1.  nthreads <= 0 uses all cores.
  * Returns 0, -1 for a table entry outside the pool, -2 when out of memory.
@@ -387,7 +395,7 @@ int orc_attention(const uint16_t* q, int32_t num_q_heads, int32_t kv_dtype,
                   const int32_t* block_tables, int32_t max_blocks,
                   const int32_t* cu_q_lens, const int32_t* context_lens, int32_t num_seqs,
                   double sm_scale, const int64_t* rows, int64_t n_rows,
-                  int64_t key_begin, int64_t key_end,
+                  int64_t key_begin, int64_t key_end, int64_t window,
                   float* out, float* lse, int32_t nthreads)
 {
     orc_attn_job* J = (orc_attn_job*)calloc(1, sizeof(orc_attn_job));
@@ -400,7 +408,8 @@ int orc_attention(const uint16_t* q, int32_t num_q_heads, int32_t kv_dtype,
     J->block_tables = block_tables; J->max_blocks = max_blocks;
     J->cu_q_lens = cu_q_lens; J->context_lens = context_lens; J->num_seqs = num_seqs;
     J->sm_scale = sm_scale; J->rows = rows; J->n_rows = n_rows;
-    J->key_begin = key_begin; J->key_end = key_end; J->out = out; J->lse = lse;
+    J->key_begin = key_begin; J->key_end = key_end; J->window = window;
+    J->out = out; J->lse = lse;
     for (int c = 0; c < 256; ++c)
         J->e4m3_table[c] = orc_e4m3_value((uint8_t)c);
     J->f16_table = (double*)malloc(sizeof(double) * 65536);

@@ -34,8 +34,9 @@ def gather_dense(kd, block_tables, b, length, block_size):
 
 
 def sdpa_reference(q_f16, num_q_heads, kd, vd, block_tables, cu_q_lens, context_lens,
-                   block_size, sm_scale):
-    """Gathered-dense causal GQA attention through torch SDPA in float64.
+                   block_size, sm_scale, window=0):
+    """Gathered-dense causal GQA attention through torch SDPA in float64;
+    window > 0 also hides keys more than window - 1 positions back.
 
     Returns out [T][Hq][D], lse [T][Hq] (natural log, from an explicit
     masked score matrix and scipy.special.logsumexp)."""
@@ -55,6 +56,8 @@ def sdpa_reference(q_f16, num_q_heads, kd, vd, block_tables, cu_q_lens, context_
         Q = q_f16[a:e].astype(np.float64)                        # [n][Hq][D]
         pos = L - n + np.arange(n)
         mask = np.arange(L)[None, :] <= pos[:, None]             # [n][L]
+        if window > 0:
+            mask &= np.arange(L)[None, :] > pos[:, None] - window
         qt = torch.from_numpy(Q).permute(1, 0, 2)                # [Hq][n][D]
         kt = torch.from_numpy(np.repeat(K, G, axis=1)).permute(1, 0, 2).contiguous()
         vt = torch.from_numpy(np.repeat(V, G, axis=1)).permute(1, 0, 2).contiguous()

@@ -256,3 +256,56 @@ def test_empty_key_window_gives_zero_and_minus_inf():
     o, l = cases.oracle_attention(w, c, key_begin=39, key_end=40)   # row 0 sits at pos 38
     assert np.all(o[0] == 0) and np.all(l[0] == -np.inf)
     assert np.all(np.isfinite(l[1]))
+
+
+# ---- sliding window (1Cat-vLLM README, "DFlash2 Long-Context Decay")
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape,window", [
+    (([40], [40], 2, 1, 8), 1),
+    (([40], [40], 2, 1, 8), 7),
+    (([37, 64, 17], [37, 3, 1], 4, 2, 8), 16),
+    (([300, 90], [8, 8], 8, 1, 128), 33),
+    (([300], [40], 8, 1, 128), 100),
+])
+def test_windowed_oracle_matches_dense_sdpa(dtype, shape, window):
+    ctx, ql, hq, hkv, d = shape
+    w = synthetic.generate(cases.spec(ctx, ql, hq=hq, hkv=hkv, d=d, seed=31 + window))
+    c = cases.oracle_cache(w, dtype)
+    sm = 1.0 / math.sqrt(d)
+    out, lse = cases.oracle_attention(w, c, sm, window=window)
+    kd, vd = refs.dequant_cache(c)
+    ro, rl = refs.sdpa_reference(w.q, hq, kd, vd, w.block_tables, w.cu_q_lens, w.context_lens,
+                                 w.spec.block_size, sm, window=window)
+    assert np.max(np.abs(out - ro)) <= 1e-6 * max(1.0, np.max(np.abs(ro)))
+    assert np.max(np.abs(lse - rl)) <= 1e-6 * max(1.0, np.max(np.abs(rl)))
+
+
+def test_window_of_one_is_the_own_token():
+    # each query sees only its own key: out = its value, lse = its score
+    w = _single_seq(30, 6)
+    c = cases.oracle_cache(w, "fp16")
+    out, lse = cases.oracle_attention(w, c, 0.5, window=1)
+    for i in range(6):
+        pos = 24 + i
+        for h in range(2):
+            assert np.array_equal(out[i, h], w.v[pos, 0].astype(np.float32))
+            s = 0.5 * float(np.dot(w.q[i, h].astype(np.float64), w.k[pos, 0].astype(np.float64)))
+            assert abs(lse[i, h] - s) < 1e-6
+
+
+def test_window_covering_the_context_changes_nothing():
+    w = synthetic.generate(cases.spec([200, 77], [5, 77], hq=4, hkv=2, d=16, seed=33))
+    c = cases.oracle_cache(w, "e4m3")
+    o0, l0 = cases.oracle_attention(w, c, 0.25)
+    o1, l1 = cases.oracle_attention(w, c, 0.25, window=200)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_window_equals_key_range_per_row():
+    # for one query token, the window is the key range [pos - W + 1, pos]
+    w = synthetic.generate(cases.spec([500], [1], hq=8, hkv=1, d=128, seed=34))
+    c = cases.oracle_cache(w, "int8")
+    o1, l1 = cases.oracle_attention(w, c, 0.088, window=64)
+    o2, l2 = cases.oracle_attention(w, c, 0.088, key_begin=500 - 64)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
