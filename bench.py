@@ -20,7 +20,8 @@ FP16 / E4M3 / INT8, and the CPU oracle timed on the host cores.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu]
 
 Profiling aids (no bench line): --prefill-only runs and times just the chunked
-prefill; --verify-only just the verification decode; --copy-calibration runs a plain 256 MiB device copy five times, the
+prefill; --verify-only just the verification and draft-window attention;
+--copy-calibration runs a plain 256 MiB device copy five times, the
 known-size kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters.
 """
 import argparse
@@ -160,6 +161,54 @@ def bench_verify(plc, synthetic, specs, K, widths=(4, 16)):
         del caches, ws, out, lse, q
         torch.cuda.empty_cache()
     res["workload"] = specs["verify"].description + "; widths as listed"
+    return res
+
+
+def bench_window(plc, synthetic, specs, K, window=2048):
+    """Draft attention (8-token blocks, sliding window) at the long-context
+    batch's contexts and at 32K, and the same calls without a window."""
+    import dataclasses
+    res = {}
+    base = specs["draft"]
+    for tag, ctx in (("ctx32k", [32768] * len(base.context_lens)), ("long", base.context_lens)):
+        sp = dataclasses.replace(base, context_lens=list(ctx))
+        log("generating draft %s" % tag)
+        w = synthetic.generate(sp)
+        s = w.spec
+        caches, bt = build_cache(plc, w, "e4m3", 8)
+        kn, vn = w.new_kv()
+        kn, vn = to_dev(kn), to_dev(vn)
+        cu, start, ctxd = to_dev(w.cu_q_lens), to_dev(w.start_pos), to_dev(w.context_lens)
+        for c in caches:
+            plc.kv_append_quant(c, kn, vn, bt, cu, start)
+        q = to_dev(w.q)
+        T = int(w.cu_q_lens[-1])
+        n = max(s.q_lens)
+        maxc = int(w.context_lens.max())
+        out = torch.empty((T, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+        lse = torch.empty((T, s.num_q_heads), dtype=torch.float32, device="cuda")
+        sm = 1.0 / math.sqrt(s.head_dim)
+        entry = {}
+        for wt in (window, 0):
+            ws = torch.zeros(plc.window_workspace_size(s.num_seqs, T, s.num_q_heads, s.num_kv_heads,
+                                                       s.head_dim, n, maxc, wt, 0),
+                             dtype=torch.uint8, device="cuda")
+
+            def f(i):
+                plc.attn_window_paged(q, caches[i % len(caches)], bt, cu, ctxd, n, maxc, wt, 0, sm,
+                                      out=out, lse=lse, workspace=ws)
+            for i in range(3):
+                f(i)
+            _, ev = graph_time(f, max(5, min(50, K // 4)), reps=2)
+            entry["window_%d_us" % wt if wt else "no_window_us"] = round(ev * 1e6, 2)
+            log("draft %s window %d: %.2f us" % (tag, wt, ev * 1e6))
+            del ws
+        res[tag] = dict(entry, context_lens=sorted(set(int(x) for x in ctx)), tokens_per_block=n)
+        del caches, out, lse, q
+        torch.cuda.empty_cache()
+    res["workload"] = base.description + "; the same blocks at 32,768-token contexts; eight " \
+        "rotated cache copies (the windows' 3 MB per call stay cache-resident, so these are " \
+        "latency figures, not HBM-bound ones)"
     return res
 
 
@@ -411,7 +460,8 @@ def main():
         print(json.dumps({"c3_prefill": bench_prefill(plc, synthetic, specs, K)}), flush=True)
         return
     if args.verify_only:
-        print(json.dumps({"verify_e4m3": bench_verify(plc, synthetic, specs, K)}), flush=True)
+        print(json.dumps({"verify_e4m3": bench_verify(plc, synthetic, specs, K),
+                          "draft_window_e4m3": bench_window(plc, synthetic, specs, K)}), flush=True)
         return
 
     # ---------------- headline: C2 decode step ----------------
@@ -503,6 +553,7 @@ def main():
                 del c
                 torch.cuda.empty_cache()
         extra["verify_e4m3"] = bench_verify(plc, synthetic, specs, K)
+        extra["draft_window_e4m3"] = bench_window(plc, synthetic, specs, K)
         result["other_workloads"] = extra
 
     if not args.no_cpu:

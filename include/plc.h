@@ -226,6 +226,29 @@ int plc_attn_verify_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
                           size_t workspace_bytes, void* stream);
 
 /*
+ * Sliding-window attention of a few query tokens per sequence (the draft
+ * model's attention: 1Cat-vLLM README, "DFlash2 Long-Context Decay", whose
+ * loop starts at the first tile the window uses; ReVolta 0.1.2 release notes,
+ * the DFlash2 drafter's 8-token blocks and 2048-token window).  Arguments and
+ * results as plc_attn_verify_paged, except that the row at position pos
+ * attends to keys max(0, pos - window_tokens + 1) .. pos only (window_tokens
+ * 0: no window, which is plc_attn_verify_paged).  Only the partitions that
+ * hold a row's window are computed, so the cost follows the window, not the
+ * context; the automatic partition size follows the window too.
+ *  workspace: plc_window_workspace_size bytes, zero-filled before first use.
+ */
+size_t plc_window_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
+                                 int32_t max_context_len, int32_t window_tokens,
+                                 int32_t partition_tokens);
+int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
+                          const int32_t* block_tables, int32_t max_blocks, const int32_t* cu_q_lens,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t total_q_tokens,
+                          int32_t max_q_len, int32_t max_context_len, int32_t window_tokens,
+                          int32_t partition_tokens, float sm_scale, float* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * First half of plc_attn_decode_paged: per-partition normalized outputs and
  * LSEs into the workspace, laid out as plc_lse_merge reads them (o_parts at
  * offset 0, lse_parts at *lse_parts_offset bytes, nparts in *nparts).

@@ -81,6 +81,11 @@ _lib.plc_verify_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _
 _lib.plc_attn_verify_paged.restype = ctypes.c_int
 _lib.plc_attn_verify_paged.argtypes = [_P, _i32, _KV, _P, _i32, _P, _P, _i32, _i32, _i32, _i32, _i32,
                                        _f32, _P, _P, _P, _sz, _P]
+_lib.plc_window_workspace_size.restype = _sz
+_lib.plc_window_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
+_lib.plc_attn_window_paged.restype = ctypes.c_int
+_lib.plc_attn_window_paged.argtypes = [_P, _i32, _KV, _P, _i32, _P, _P, _i32, _i32, _i32, _i32, _i32,
+                                       _i32, _f32, _P, _P, _P, _sz, _P]
 _lib.plc_lse_merge.restype = ctypes.c_int
 _lib.plc_lse_merge.argtypes = [_P, _P, _i32, _i32, _i32, _P, _P, _P]
 _lib.plc_debug_e4m3_to_f16.restype = ctypes.c_int
@@ -333,6 +338,13 @@ def verify_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads, h
                                               partition_tokens))
 
 
+def window_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim, max_q_len,
+                          max_context_len, window_tokens, partition_tokens=0) -> int:
+    return int(_lib.plc_window_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads,
+                                              head_dim, max_q_len, max_context_len, window_tokens,
+                                              partition_tokens))
+
+
 def attn_verify_paged(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor,
                       cu_q_lens: torch.Tensor, context_lens: torch.Tensor, max_q_len: int,
                       max_context_len: int, partition_tokens: int = 0,
@@ -341,6 +353,18 @@ def attn_verify_paged(q: torch.Tensor, cache: KVCache, block_tables: torch.Tenso
     """Verification decode: a few query tokens per sequence (the last n_b
     positions), causal among themselves, split-KV with the merge in the same
     launch; q fp16 [T][Hq][D] -> (out fp32 [T][Hq][D], lse fp32 [T][Hq])."""
+    return attn_window_paged(q, cache, block_tables, cu_q_lens, context_lens, max_q_len,
+                             max_context_len, 0, partition_tokens, sm_scale, out, lse, workspace,
+                             stream)
+
+
+def attn_window_paged(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor,
+                      cu_q_lens: torch.Tensor, context_lens: torch.Tensor, max_q_len: int,
+                      max_context_len: int, window_tokens: int, partition_tokens: int = 0,
+                      sm_scale: Optional[float] = None, out=None, lse=None, workspace=None,
+                      stream=None):
+    """As attn_verify_paged, with the row at position pos limited to keys
+    pos - window_tokens + 1 .. pos (0: no window)."""
     T, Hq, D = q.shape
     _need(q, "q", torch.float16)
     _need(block_tables, "block_tables", torch.int32)
@@ -354,18 +378,18 @@ def attn_verify_paged(q: torch.Tensor, cache: KVCache, block_tables: torch.Tenso
     _need(out, "out", torch.float32, (T, Hq, D))
     _need(lse, "lse", torch.float32, (T, Hq))
     if workspace is None:
-        need = verify_workspace_size(B, T, Hq, cache.num_kv_heads, D, int(max_q_len),
-                                     int(max_context_len), int(partition_tokens))
+        need = window_workspace_size(B, T, Hq, cache.num_kv_heads, D, int(max_q_len),
+                                     int(max_context_len), int(window_tokens), int(partition_tokens))
         # zero-filled: the merge's completion counters start at zero
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
-    _check(_lib.plc_attn_verify_paged(_ptr(q), Hq, cache.desc(), _ptr(block_tables),
+    _check(_lib.plc_attn_window_paged(_ptr(q), Hq, cache.desc(), _ptr(block_tables),
                                       block_tables.shape[1], _ptr(cu_q_lens), _ptr(context_lens), B, T,
-                                      int(max_q_len), int(max_context_len), int(partition_tokens),
-                                      float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
-                                      workspace.numel(), _stream(stream)))
+                                      int(max_q_len), int(max_context_len), int(window_tokens),
+                                      int(partition_tokens), float(sm_scale), _ptr(out), _ptr(lse),
+                                      _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
 
 

@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "../../include/plc.h"
@@ -152,12 +153,27 @@ int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
     p.cu_q_lens = nullptr;
     p.max_q_len = 1;
     p.ncg = 1;
+    p.window = 0;
     return PLC_OK;
 }
 
 // rows of one (sequence, KV head) in groups of 16, one workgroup column each
 int32_t verify_row_groups(int32_t num_q_heads, int32_t num_kv_heads, int32_t max_q_len) {
     return (max_q_len * (num_q_heads / num_kv_heads) + 15) / 16;
+}
+
+// Partition size and partitions per sequence for a few-query-token call.
+// Without a window the keys are the whole context.  With one, a sequence's
+// rows need at most window + max_q_len - 1 keys, which touch at most one
+// partition more than they fill; the default size follows that span.
+void mq_partitions(int32_t groups, int32_t num_kv_heads, int32_t max_q_len, int32_t max_context_len,
+                   int32_t window, int32_t partition_tokens, int32_t* P, int32_t* nparts) {
+    const int64_t span = window > 0 ? std::min<int64_t>(max_context_len, (int64_t)window + max_q_len - 1)
+                                    : max_context_len;
+    *P = resolve_partition(groups, num_kv_heads, (int32_t)span, partition_tokens);
+    const int64_t all = max_context_len > 0 ? (max_context_len + *P - 1) / *P : 1;
+    *nparts = (int32_t)(window > 0 ? std::min<int64_t>(all, (span + *P - 1) / *P + 1) : all);
+    if (*nparts < 1) *nparts = 1;
 }
 
 }  // namespace
@@ -310,16 +326,19 @@ int plc_attn_decode_append(const void* q, const void* k_new, const void* v_new,
                       "decode-append launch");
 }
 
-size_t plc_verify_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
+size_t plc_window_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
-                                 int32_t max_context_len, int32_t partition_tokens) {
+                                 int32_t max_context_len, int32_t window_tokens,
+                                 int32_t partition_tokens) {
     if (num_seqs <= 0 || total_q_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
         num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_q_len < 1 ||
-        max_q_len > PLC_VERIFY_MAX_Q_LEN || max_context_len < 0)
+        max_q_len > PLC_VERIFY_MAX_Q_LEN || max_context_len < 0 || window_tokens < 0 ||
+        partition_tokens < 0)
         return 0;
     const int32_t ncg = verify_row_groups(num_q_heads, num_kv_heads, max_q_len);
-    const int32_t P = resolve_partition(num_seqs * ncg, num_kv_heads, max_context_len, partition_tokens);
-    const int64_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
+    int32_t P = 0, nparts = 0;
+    mq_partitions(num_seqs * ncg, num_kv_heads, max_q_len, max_context_len, window_tokens,
+                  partition_tokens, &P, &nparts);
     const size_t rows = (size_t)total_q_tokens * num_q_heads;
     // partial outputs and LSEs per query row, one completion counter per
     // (sequence, KV head, row group)
@@ -327,12 +346,19 @@ size_t plc_verify_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32
            align_up((size_t)num_seqs * num_kv_heads * ncg * sizeof(int32_t));
 }
 
-int plc_attn_verify_paged(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
+size_t plc_verify_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
+                                 int32_t max_context_len, int32_t partition_tokens) {
+    return plc_window_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                                     max_q_len, max_context_len, 0, partition_tokens);
+}
+
+int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
                           const int32_t* block_tables, int32_t max_blocks, const int32_t* cu_q_lens,
                           const int32_t* context_lens, int32_t num_seqs, int32_t total_q_tokens,
-                          int32_t max_q_len, int32_t max_context_len, int32_t partition_tokens,
-                          float sm_scale, float* out, float* lse, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          int32_t max_q_len, int32_t max_context_len, int32_t window_tokens,
+                          int32_t partition_tokens, float sm_scale, float* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
     int rc;
     if ((rc = check_cache(kv))) return rc;
     if ((rc = check_heads(num_q_heads, kv))) return rc;
@@ -345,6 +371,8 @@ int plc_attn_verify_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     if (max_q_len > max_context_len)
         return fail(PLC_ERR_INVALID_ARG, "max_q_len %d exceeds max_context_len %d", max_q_len,
                     max_context_len);
+    if (window_tokens < 0)
+        return fail(PLC_ERR_INVALID_ARG, "window_tokens %d is negative (0: no window)", window_tokens);
     if (total_q_tokens == 0) return PLC_OK;
     if (!q || !block_tables || !cu_q_lens || !context_lens || !out || !lse)
         return fail(PLC_ERR_INVALID_ARG, "q / block_tables / cu_q_lens / context_lens / out / lse is NULL");
@@ -354,13 +382,15 @@ int plc_attn_verify_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
         return fail(PLC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
     const int32_t ncg = verify_row_groups(num_q_heads, kv->num_kv_heads, max_q_len);
-    const int32_t P = resolve_partition(num_seqs * ncg, kv->num_kv_heads, max_context_len, partition_tokens);
-    const size_t need = plc_verify_workspace_size(num_seqs, total_q_tokens, num_q_heads, kv->num_kv_heads,
-                                                  kv->head_dim, max_q_len, max_context_len, P);
+    int32_t P = 0, nparts = 0;
+    mq_partitions(num_seqs * ncg, kv->num_kv_heads, max_q_len, max_context_len, window_tokens,
+                  partition_tokens, &P, &nparts);
+    const size_t need = plc_window_workspace_size(num_seqs, total_q_tokens, num_q_heads,
+                                                  kv->num_kv_heads, kv->head_dim, max_q_len,
+                                                  max_context_len, window_tokens, P);
     if (!workspace || workspace_bytes < need)
         return fail(PLC_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
                     workspace_bytes, workspace, need);
-    const int32_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
     const size_t rows = (size_t)total_q_tokens * num_q_heads;
     plc::DecodeParams p;
     p.q = q;
@@ -386,7 +416,21 @@ int plc_attn_verify_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     p.cu_q_lens = cu_q_lens;
     p.max_q_len = max_q_len;
     p.ncg = ncg;
-    return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)), "verify launch");
+    p.window = window_tokens;
+    return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)),
+                      window_tokens > 0 ? "window launch" : "verify launch");
+}
+
+int plc_attn_verify_paged(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
+                          const int32_t* block_tables, int32_t max_blocks, const int32_t* cu_q_lens,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t total_q_tokens,
+                          int32_t max_q_len, int32_t max_context_len, int32_t partition_tokens,
+                          float sm_scale, float* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    return plc_attn_window_paged(q, num_q_heads, kv, block_tables, max_blocks, cu_q_lens, context_lens,
+                                 num_seqs, total_q_tokens, max_q_len, max_context_len, 0,
+                                 partition_tokens, sm_scale, out, lse, workspace, workspace_bytes,
+                                 stream);
 }
 
 int plc_lse_merge(const float* o_parts, const float* lse_parts, int32_t rows, int32_t nparts,

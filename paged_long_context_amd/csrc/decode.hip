@@ -240,27 +240,31 @@ struct WaveState {
 // limit) (tok1 itself for a one-token decode).  V validity (inside the
 // partition, on a valid page) is a property of the token, shared by every
 // row, and is only needed for a partial chunk; the causal limit masks scores.
-template <int KV>
-__device__ __forceinline__ void token_ok(bool v[8], int ctok, int lim, int valid_blk, int g) {
+// With LO, tokens below lo are excluded too (a sliding window's start).
+template <bool LO>
+__device__ __forceinline__ void token_ok(bool v[8], int ctok, int lo, int lim, int valid_blk, int g) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int pg = e >> 2;
-        v[e] = (ctok + 16 * pg + 4 * g + (e & 3) < lim) && ((valid_blk >> pg) & 1);
+        const int t = ctok + 16 * pg + 4 * g + (e & 3);
+        v[e] = (t < lim) && (!LO || t >= lo) && ((valid_blk >> pg) & 1);
     }
 }
 
-template <int KV, int NW>
+// LO: the lane's row also ignores keys below lo1 (its sliding window's start).
+template <int KV, int NW, bool LO>
 __device__ __forceinline__ void process_chunk(WaveState& st, Chunk<KV>& cur, const f16x8 qop[4],
-                                              float cscale, int ctok, int tok1, int lim1, int g) {
+                                              float cscale, int ctok, int tok1, int lo1, int lim1,
+                                              int g) {
     using Dk = Decode<KV, NW>;
     // scored tokens of the lane's eight t(g, e)
     bool ok[8];
-    token_ok<KV>(ok, ctok, lim1, cur.valid_blk, g);
+    token_ok<LO>(ok, ctok, lo1, lim1, cur.valid_blk, g);
     const bool partial = (ctok + 32 > tok1) || (cur.valid_blk != 3);
     if constexpr (KV != KV_FP16)
         if (partial) {
             bool vok[8];
-            token_ok<KV>(vok, ctok, tok1, cur.valid_blk, g);
+            token_ok<false>(vok, ctok, 0, tok1, cur.valid_blk, g);
             Dk::mask_v(cur, vok);
         }
 
@@ -312,7 +316,7 @@ __device__ __forceinline__ void process_chunk(WaveState& st, Chunk<KV>& cur, con
     if constexpr (KV == KV_FP16)
         if (partial) {
             bool vok[8];
-            token_ok<KV>(vok, ctok, tok1, cur.valid_blk, g);
+            token_ok<false>(vok, ctok, 0, tok1, cur.valid_blk, g);
 #pragma unroll
             for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -452,16 +456,14 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     // lengths beyond the host-stated bound are clamped so that no page id
     // outside the table is ever read
     const int P = p.partition_tokens;
-    const int blk0 = part * (P / BS);
+    int blk0 = part * (P / BS);                                  // MQ: set once L is known
     const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
     // The first segment's page ids do not depend on the sequence length:
     // fetch them now, alongside the length (entries past the end are masked
     // once the length is known; the index stays inside the table row).
     const int tb0 = 2 * (cw + (lane >> 1) * NW) + (lane & 1);
-    const int tbl0 = bt[min(blk0 + tb0, p.max_blocks - 1)];
+    int tbl0 = MQ ? 0 : bt[min(blk0 + tb0, p.max_blocks - 1)];
     const int L = max(0, min(p.context_lens[b], p.max_context_len));
-    const int nparts_b = (L + P - 1) / P;
-    const int tok0 = part * P;
     const int nparts = p.nparts;
     // this workgroup's query rows: NC columns of the 16-wide N tile
     int n = 1;
@@ -473,6 +475,17 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     const RowMap rm{qa * Hq + kvh * G, Hq, 16 * cg, __builtin_ctz(G)};
     const int NC = MQ ? min(16, n * G - 16 * cg) : G;
     if (MQ && NC <= 0) return;                                   // no rows: no partials, no merge
+    // Sliding window (MQ, p.window > 0): row j sees keys from L - n + j -
+    // window + 1 on, so no row needs a key below lo_min (row 0's start); the
+    // workgroups' partition index counts from the partition that holds it.
+    int lo_min = 0, first_part = 0;
+    if constexpr (MQ)
+        if (p.window > 0) {
+            lo_min = max(0, L - n + 1 - p.window);
+            first_part = lo_min / P;
+        }
+    const int nparts_b = (L + P - 1) / P - first_part;
+    int tok0 = (part + first_part) * P;
 
     if (part >= nparts_b) {                                      // partition past the end
         if (p.counters) {
@@ -494,6 +507,13 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
         return;
     }
     const int tok1 = min(tok0 + P, L);
+    if constexpr (MQ) {
+        // skip the chunks below every row's window, then fetch the first
+        // segment's page ids (deferred until the length was known)
+        tok0 += 32 * (max(0, lo_min - tok0) / 32);
+        blk0 = tok0 / BS;
+        tbl0 = bt[min(blk0 + tb0, p.max_blocks - 1)];
+    }
     const int nblk = (tok1 - tok0 + BS - 1) / BS;
     const int nchunks = (nblk + 1) / 2;
 
@@ -540,6 +560,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     f16x8 qop[4];
     const int lim = i < NC ? L - n + 1 + ((16 * cg + i) >> rm.gshift) : 0;
     const int lim1 = MQ ? min(lim, tok1) : tok1;       // and inside the partition
+    const int lo1 = p.window > 0 ? lim - p.window : 0;  // the row's window start (MQ)
     {
         const f16* q = static_cast<const f16*>(p.q) + rm.row(i < NC ? i : 0) * D;
 #pragma unroll
@@ -619,7 +640,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             Dk::read(c, ma, &s_dma[wave][0][0], kofs, vofs);
-            process_chunk<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, lim1, g);
+            process_chunk<KV, NW, MQ>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, lo1, lim1, g);
             if (k + 1 >= segn) break;
             if (k + 2 < segn) {
                 issue(ma, 0, k + 2);
@@ -628,7 +649,8 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             Dk::read(c, mb, &s_dma[wave][1][0], kofs, vofs);
-            process_chunk<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k + 1) * NW), tok1, lim1, g);
+            process_chunk<KV, NW, MQ>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k + 1) * NW), tok1, lo1, lim1,
+                                      g);
         }
     }
     __syncthreads();                                   // the merge below reuses the DMA buffers

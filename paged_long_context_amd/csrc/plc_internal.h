@@ -50,6 +50,10 @@ struct DecodeParams {
     const int32_t* cu_q_lens;
     int32_t max_q_len;
     int32_t ncg;
+    // with cu_q_lens: > 0 limits the row at position pos to keys
+    // pos - window + 1 .. pos, and partition k of a sequence is then the k-th
+    // one from the partition holding its first query's first key
+    int32_t window;
 };
 
 hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s);

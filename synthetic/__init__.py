@@ -250,6 +250,12 @@ def named_specs() -> Dict[str, Spec]:
         seed=BASE_SEED + 6,
         description="verification decode: 8 x 32,768 context, 4 drafted tokens per sequence "
                     "(causal among themselves), 8 q / 1 kv, E4M3, partitions of 2,048")
+    # and the draft model's attention: 8-token blocks over the long-context
+    # batch's contexts, attending through a 2,048-token sliding window
+    s["draft"] = Spec(
+        name="draft", context_lens=[524288] * 2 + [262144] * 4, q_lens=[8] * 6, seed=BASE_SEED + 7,
+        description="draft attention: 2 x 524,288 + 4 x 262,144 context, 8-token blocks, "
+                    "2,048-token sliding window, 8 q / 1 kv, E4M3")
     return s
 
 
