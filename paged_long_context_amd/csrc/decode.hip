@@ -60,7 +60,6 @@ struct Decode {
     //   c ^ s; V (whole 256-byte rows per 16-lane group already) stays in
     //   registers.
     struct Meta {
-        f32x4 ks[2], vs[2];          // INT8 per-token scales, as in Chunk
         u32x4 v16[(KV == KV_FP16) ? 8 : 1];   // FP16 V rows, as in Chunk
         int valid_blk;
     };
@@ -92,7 +91,8 @@ struct Decode {
                      "global_load_lds_dwordx4 %2, off nt\n\ts_mov_b32 m0, %0"
                      : "=&s"(saved) : "s"(base), "v"(src) : "memory");
     }
-    __device__ __forceinline__ static void issue(Meta& m, uint8_t* lbuf, const DecodeParams& p, int kvh, int pb0,
+    __device__ __forceinline__ static void issue(Meta& m, uint8_t* lbuf, f32x4* sbuf, const DecodeParams& p,
+                                                 int kvh, int pb0,
                                                  int pb1, bool has1, int lane, const int src[kDmaPerPage]) {
         const int g = lane >> 4, i = lane & 15;
         const int nb = p.kv.num_blocks;
@@ -125,22 +125,28 @@ struct Decode {
             }
         }
         if constexpr (KV == KV_INT8) {
-#pragma unroll
-            for (int pg = 0; pg < 2; ++pg) {
-                const int64_t srow = ((int64_t)pbs[pg] * Hkv + kvh) * BS + 4 * g;
-                m.ks[pg] = *reinterpret_cast<const f32x4*>(p.kv.k_scale + srow);
-                m.vs[pg] = *reinterpret_cast<const f32x4*>(p.kv.v_scale + srow);
-            }
+            // the two pages' per-token scales by one more DMA: lane l (mod
+            // 16) moves 16 bytes (4 tokens) of [K | V][page][4 tokens x 4]
+            // into slot l of sbuf; lanes 16..63 repeat lanes 0..15 into
+            // slots nothing reads
+            const int sl = lane & 15, spg = (sl >> 2) & 1;
+            const float* sc = ((sl >> 3) ? p.kv.v_scale : p.kv.k_scale) +
+                              ((int64_t)pbs[spg] * Hkv + kvh) * BS + 4 * (sl & 3);
+            dma16(reinterpret_cast<const uint8_t*>(sc), reinterpret_cast<uint8_t*>(sbuf));
         }
+        (void)g;
+        (void)i;
+        (void)sbuf;
     }
     // vector memory operations issue() puts in flight
-    static constexpr int kIssueOps = (KV == KV_FP16) ? 16 : (KV == KV_INT8) ? 12 : 8;
+    static constexpr int kIssueOps = (KV == KV_FP16) ? 16 : (KV == KV_INT8) ? 9 : 8;
     // The chunk's operands from LDS.  8-bit: lane (i, g) reads token row i's
     // chunks 4h + g of K (kofs[h]) and the 8 bytes d = 8i.. of V tokens
     // 16(e>>2) + 4g + (e&3) (vofs[e&3]).  FP16: token row i's chunks
     // 8h + 2g + sub of K (kofs[2h + sub]).
-    __device__ __forceinline__ static void read(Chunk<KV>& c, const Meta& m, const uint8_t* lbuf, const int kofs[4],
-                                                const int vofs[4]) {
+    __device__ __forceinline__ static void read(Chunk<KV>& c, const Meta& m, const uint8_t* lbuf,
+                                                const f32x4* sbuf, const int kofs[4], const int vofs[4],
+                                                int g) {
         if constexpr (KV == KV_FP16) {
 #pragma unroll
             for (int pg = 0; pg < 2; ++pg)
@@ -159,8 +165,14 @@ struct Decode {
             for (int e = 0; e < 8; ++e)
                 c.v8[e] = *reinterpret_cast<const u32x2*>(lbuf + 4096 + 2048 * (e >> 2) + vofs[e & 3]);
         }
-        c.ks[0] = m.ks[0]; c.ks[1] = m.ks[1];
-        c.vs[0] = m.vs[0]; c.vs[1] = m.vs[1];
+        if constexpr (KV == KV_INT8) {                 // scales of tokens 4g..4g+3 of each page
+#pragma unroll
+            for (int pg = 0; pg < 2; ++pg) {
+                c.ks[pg] = sbuf[4 * pg + g];
+                c.vs[pg] = sbuf[4 * (2 + pg) + g];
+            }
+        }
+        (void)g;
         c.valid_blk = m.valid_blk;
     }
 
@@ -439,6 +451,8 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     // Pages stream through per-wave LDS buffers (two 8 KiB chunks per wave);
     // the wave merge and the fused merge reuse that space afterwards.
     __shared__ __attribute__((aligned(16))) uint8_t s_dma[NW][2][8192];
+    // INT8 per-token scales of each buffer's chunk (slots 0..15 used)
+    __shared__ __attribute__((aligned(16))) f32x4 s_scl[KV == KV_INT8 ? NW : 1][2][KV == KV_INT8 ? 64 : 1];
     float* smem = reinterpret_cast<float*>(&s_dma[0][0][0]);
     __shared__ int s_last;
     const int part = blockIdx.x, b = blockIdx.z;
@@ -626,7 +640,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
         // (none after the segment's last chunk, so no DMA outlives it)
         auto issue = [&](typename Dk::Meta& m, int b, int k) __attribute__((always_inline)) {
             const int ch = cw + (seg + k) * NW;
-            Dk::issue(m, &s_dma[wave][b][0], p, kvh, __builtin_amdgcn_readlane(tbl, 2 * k),
+            Dk::issue(m, &s_dma[wave][b][0], &s_scl[KV == KV_INT8 ? wave : 0][b][0], p, kvh, __builtin_amdgcn_readlane(tbl, 2 * k),
                       __builtin_amdgcn_readlane(tbl, 2 * k + 1), 2 * ch + 1 < nblk, lane, dsrc);
         };
         typename Dk::Meta ma, mb;
@@ -639,7 +653,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
             } else {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
-            Dk::read(c, ma, &s_dma[wave][0][0], kofs, vofs);
+            Dk::read(c, ma, &s_dma[wave][0][0], &s_scl[KV == KV_INT8 ? wave : 0][0][0], kofs, vofs, g);
             process_chunk<KV, NW, MQ>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, lo1, lim1, g);
             if (k + 1 >= segn) break;
             if (k + 2 < segn) {
@@ -648,7 +662,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
             } else {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
-            Dk::read(c, mb, &s_dma[wave][1][0], kofs, vofs);
+            Dk::read(c, mb, &s_dma[wave][1][0], &s_scl[KV == KV_INT8 ? wave : 0][1][0], kofs, vofs, g);
             process_chunk<KV, NW, MQ>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k + 1) * NW), tok1, lo1, lim1,
                                       g);
         }
