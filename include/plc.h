@@ -29,6 +29,14 @@
  *    trusted within the bounds the host arguments state.
  *  - Supported shapes: head_dim 128, block_size 16, num_q_heads a multiple of
  *    num_kv_heads with a group size G = Hq/Hkv of 1, 2, 4, 8 or 16.
+ *  - head_dim 256 (1Cat-vLLM README, Layer 2 "D256 Split-D": the head is
+ *    processed as two 128-wide halves; "GQA Multi-Head Packing": six query
+ *    heads per KV head) is taken by plc_kv_append_quant,
+ *    plc_attn_decode_partials, plc_attn_decode_paged and
+ *    plc_attn_decode_append, with any group size G from 1 to 16.  There the
+ *    decode writes partials and merges them in a second kernel (the one of
+ *    plc_lse_merge), so the workspace counters are unused.  The other entry
+ *    points refuse head_dim 256 with PLC_ERR_UNSUPPORTED.
  */
 #ifndef PLC_H
 #define PLC_H

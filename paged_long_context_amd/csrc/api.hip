@@ -26,7 +26,8 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
-constexpr int kHeadDim = 128;
+constexpr int kHeadDim = 128;       // every entry point
+constexpr int kHeadDimWide = 256;   // KV append and one-token decode (split in two 128 halves)
 constexpr int kBlockSize = 16;
 constexpr size_t kAlign = 256;
 
@@ -37,9 +38,9 @@ int check_cache(const plc_kv_cache* kv) {
     if (kv->dtype != PLC_KV_FP16 && kv->dtype != PLC_KV_E4M3 && kv->dtype != PLC_KV_INT8)
         return fail(PLC_ERR_UNSUPPORTED, "kv dtype %d is not one of FP16(0), E4M3(1), INT8(2)",
                     kv->dtype);
-    if (kv->head_dim != kHeadDim)
-        return fail(PLC_ERR_UNSUPPORTED, "head_dim %d: kernels are built for %d", kv->head_dim,
-                    kHeadDim);
+    if (kv->head_dim != kHeadDim && kv->head_dim != kHeadDimWide)
+        return fail(PLC_ERR_UNSUPPORTED, "head_dim %d: kernels are built for %d and %d", kv->head_dim,
+                    kHeadDim, kHeadDimWide);
     if (kv->block_size != kBlockSize)
         return fail(PLC_ERR_UNSUPPORTED, "block_size %d: kernels are built for %d", kv->block_size,
                     kBlockSize);
@@ -60,8 +61,21 @@ int check_heads(int32_t num_q_heads, const plc_kv_cache* kv) {
         return fail(PLC_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
                     num_q_heads, kv->num_kv_heads);
     const int G = num_q_heads / kv->num_kv_heads;
+    if (kv->head_dim == kHeadDimWide) {
+        // the wide decode packs the group into one 16-column MFMA tile
+        if (G > 16) return fail(PLC_ERR_UNSUPPORTED, "GQA group size %d: head_dim 256 supports 1..16", G);
+        return PLC_OK;
+    }
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
         return fail(PLC_ERR_UNSUPPORTED, "GQA group size %d: supported are 1, 2, 4, 8, 16", G);
+    return PLC_OK;
+}
+
+// Entry points built for head dim 128 only.
+int check_narrow(const plc_kv_cache* kv, const char* what) {
+    if (kv->head_dim != kHeadDim)
+        return fail(PLC_ERR_UNSUPPORTED, "%s is built for head_dim %d only (got %d)", what, kHeadDim,
+                    kv->head_dim);
     return PLC_OK;
 }
 
@@ -85,6 +99,7 @@ plc::KvView view(const plc_kv_cache* kv) {
     v.v_scale = kv->v_scale;
     v.num_blocks = kv->num_blocks;
     v.num_kv_heads = kv->num_kv_heads;
+    v.head_dim = kv->head_dim;
     v.dtype = kv->dtype;
     return v;
 }
@@ -222,6 +237,7 @@ int plc_attn_prefill_paged(const void* q, int32_t num_q_heads, const plc_kv_cach
                            void* stream) {
     int rc;
     if ((rc = check_cache(kv))) return rc;
+    if ((rc = check_narrow(kv, "plc_attn_prefill_paged"))) return rc;
     if ((rc = check_heads(num_q_heads, kv))) return rc;
     if ((rc = check_lengths(num_seqs, max_blocks, max_context_len, kv->block_size))) return rc;
     if (total_q_tokens < 0 || max_q_len < 0)
@@ -363,6 +379,7 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
                           void* workspace, size_t workspace_bytes, void* stream) {
     int rc;
     if ((rc = check_cache(kv))) return rc;
+    if ((rc = check_narrow(kv, "verification / window attention"))) return rc;
     if ((rc = check_heads(num_q_heads, kv))) return rc;
     if ((rc = check_lengths(num_seqs, max_blocks, max_context_len, kv->block_size))) return rc;
     if (total_q_tokens < 0)

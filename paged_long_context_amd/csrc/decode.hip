@@ -44,9 +44,13 @@ struct Chunk {
     int valid_blk;                  // bit p set when page p is inside the pool
 };
 
-template <int KV, int NW>
+// DH: the cache's head dim (row length in elements).  A page of head dim 256 is
+// read as two halves of 128 (Split-D), each laid out in LDS like a whole
+// 128-wide page; hoff selects the half.
+template <int KV, int NW, int DH = 128>
 struct Decode {
     static constexpr int EB = ElemBytes<KV>::value;
+    static constexpr int RB = DH * EB;              // bytes per cache row
 
     // ---- Pages reach a per-wave LDS buffer (two 8 KiB chunk buffers per wave,
     // ping-pong) by DMA: global_load_lds, 16 bytes per lane, every instruction
@@ -71,10 +75,10 @@ struct Decode {
     __device__ __forceinline__ static int dma_src(int lane, int q) {
         if constexpr (KV == KV_FP16) {
             const int s = 4 * q + (lane >> 4);
-            return s * (D * 2) + 16 * ((lane & 15) ^ s);
+            return s * RB + 16 * ((lane & 15) ^ s);
         } else {
             const int s = 8 * q + (lane >> 3);
-            return swap02(s) * D + 16 * ((lane & 7) ^ kap(s));
+            return swap02(s) * RB + 16 * ((lane & 7) ^ kap(s));
         }
     }
     // One global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS
@@ -93,7 +97,8 @@ struct Decode {
     }
     __device__ __forceinline__ static void issue(Meta& m, uint8_t* lbuf, f32x4* sbuf, const DecodeParams& p,
                                                  int kvh, int pb0,
-                                                 int pb1, bool has1, int lane, const int src[kDmaPerPage]) {
+                                                 int pb1, bool has1, int lane, const int src[kDmaPerPage],
+                                                 int hoff = 0, bool scales = true) {
         const int g = lane >> 4, i = lane & 15;
         const int nb = p.kv.num_blocks;
         m.valid_blk = ((pb0 >= 0 && pb0 < nb) ? 1 : 0) | ((has1 && pb1 >= 0 && pb1 < nb) ? 2 : 0);
@@ -101,7 +106,7 @@ struct Decode {
         const int Hkv = p.kv.num_kv_heads;
 #pragma unroll
         for (int pg = 0; pg < 2; ++pg) {
-            const int64_t base = ((int64_t)pbs[pg] * Hkv + kvh) * (BS * D * EB);
+            const int64_t base = ((int64_t)pbs[pg] * Hkv + kvh) * (BS * RB) + hoff;
             const uint8_t* kp = static_cast<const uint8_t*>(p.kv.k) + base;
             const uint8_t* vp = static_cast<const uint8_t*>(p.kv.v) + base;
             if constexpr (KV == KV_FP16) {
@@ -119,12 +124,12 @@ struct Decode {
             // V: token 4g + e%4 of page e/4, d = 8i..8i+7, one 16-byte load each
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int64_t base = ((int64_t)pbs[e >> 2] * Hkv + kvh) * (BS * D * EB);
+                const int64_t base = ((int64_t)pbs[e >> 2] * Hkv + kvh) * (BS * RB) + hoff;
                 m.v16[e] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(p.kv.v) + base +
-                                                           (4 * g + (e & 3)) * (D * EB) + 16 * i);
+                                                           (4 * g + (e & 3)) * RB + 16 * i);
             }
         }
-        if constexpr (KV == KV_INT8) {
+        if constexpr (KV == KV_INT8) if (scales) {
             // the two pages' per-token scales by one more DMA: lane l (mod
             // 16) moves 16 bytes (4 tokens) of [K | V][page][4 tokens x 4]
             // into slot l of sbuf; lanes 16..63 repeat lanes 0..15 into
@@ -743,6 +748,308 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     merge_group<NW>(p, rm, NC, nparts_b, tid, smem);
 }
 
+// ---------------------------------------------------------------- head dim 256
+// Split-D (1Cat-vLLM README, Layer 2 "D256 Split-D"): a 256-wide head is two
+// 128-wide halves.  Each 32-token chunk arrives as two half-chunks in the
+// 128-wide LDS layout; the scores sum both halves' QK^T before the softmax,
+// and PV runs per half into its own accumulators, so the probabilities are
+// computed once for the whole row.  The GQA group (any size up to 16; the
+// pages pack six heads, Layer 2 "GQA Multi-Head Packing") is the MFMA N
+// dimension, as in the 128-wide kernel.  One query token per sequence;
+// partials only (the merge is plc_lse_merge's kernel).
+struct WaveState2 {
+    float m, l;
+    f32x4 acc[2][8];               // half h: O^T[d = 128h + 32g + 8r + c][head i] in acc[h][c][r]
+};
+
+template <int KV, int NW>
+__device__ __forceinline__ void process_chunk_d256(WaveState2& st, Chunk<KV> cur[2], const f16x8 qop[2][4],
+                                                   float cscale, int ctok, int tok1, int g) {
+    using Dk = Decode<KV, NW, 256>;
+    bool ok[8];
+    token_ok<false>(ok, ctok, 0, tok1, cur[0].valid_blk, g);
+    const bool partial = (ctok + 32 > tok1) || (cur[0].valid_blk != 3);
+    if constexpr (KV != KV_FP16)
+        if (partial) {
+            Dk::mask_v(cur[0], ok);                 // one-token decode: key validity is the mask
+            Dk::mask_v(cur[1], ok);
+        }
+    float x[8];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+        f32x4 s = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f16x8 kop[4];
+            Dk::k_operands(cur[h], pg, kop);
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) s = mfma16(kop[kc], qop[h][kc], s);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float sc = cscale;
+            if constexpr (KV == KV_INT8) sc *= cur[0].ks[pg][r];
+            x[4 * pg + r] = s[r] * sc;
+        }
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        x[e] = ok[e] ? x[e] : -__builtin_inff();
+        mx = fmaxf(mx, x[e]);
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+    const float alpha = fast_exp2(st.m - m_use);
+    float psum = 0.0f;
+    f16x8 pop;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float pe = fast_exp2(x[e] - m_use);
+        psum += pe;
+        if constexpr (KV == KV_INT8) pe *= cur[0].vs[e >> 2][e & 3] * 256.0f;
+        pop[e] = (f16)pe;
+    }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st.acc[h][c] *= alpha;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        f16x8 vt[8];
+        Dk::v_operands(cur[h], vt);
+        if constexpr (KV == KV_FP16)
+            if (partial) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vt[c][e] = ok[e] ? vt[c][e] : (f16)0.0f;
+            }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st.acc[h][c] = mfma16(vt[c], pop, st.acc[h][c]);
+    }
+}
+
+template <int KV, int NW>
+__global__ __launch_bounds__(64 * NW) void paged_decode256_kernel(DecodeParams p) {
+    using Dk = Decode<KV, NW, 256>;
+    constexpr int DW = 256;
+    // [wave][buffer][half]: two buffers in ping-pong, each chunk's two halves
+    __shared__ __attribute__((aligned(16))) uint8_t s_dma[NW][2][2][8192];
+    __shared__ __attribute__((aligned(16))) f32x4 s_scl[KV == KV_INT8 ? NW : 1][2][KV == KV_INT8 ? 64 : 1];
+    float* smem = reinterpret_cast<float*>(&s_dma[0][0][0][0]);
+    const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cw = NW - 1 - wave;
+    const int g = lane >> 4, i = lane & 15;
+    const int Hq = p.num_q_heads, Hkv = p.kv.num_kv_heads, G = Hq / Hkv;
+    const int P = p.partition_tokens;
+    const int blk0 = part * (P / BS);
+    const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
+    const int tb0 = 2 * (cw + (lane >> 1) * NW) + (lane & 1);
+    const int tbl0 = bt[min(blk0 + tb0, p.max_blocks - 1)];
+    const int L = max(0, min(p.context_lens[b], p.max_context_len));
+    const int nparts = p.nparts;
+    const int nparts_b = (L + P - 1) / P;
+    const int64_t row0 = (int64_t)b * Hq + (int64_t)kvh * G;      // the group's first query head's row
+    if (part >= nparts_b) {                                        // partition past the end
+        for (int idx = tid; idx < G * DW; idx += 64 * NW) {
+            const int j = idx / DW, d = idx % DW;
+            p.o_parts[((row0 + j) * nparts + part) * DW + d] = 0.0f;
+            if (d == 0) p.lse_parts[(row0 + j) * nparts + part] = -__builtin_inff();
+        }
+        return;
+    }
+    const int tok0 = part * P, tok1 = min(tok0 + P, L);
+    const int nblk = (tok1 - tok0 + BS - 1) / BS;
+    const int nchunks = (nblk + 1) / 2;
+
+    if (p.k_new != nullptr && part == (L - 1) / P) {
+        // fused append of the step's token (position L - 1), quantized as
+        // plc_kv_append_quant does: wave 0, 32 lanes per K / V row; every
+        // wave waits for the stores before it loads
+        if (wave == 0) {
+            const int which = lane >> 5, sl = lane & 31;
+            const int pos = L - 1;
+            const int pg = bt[pos / BS];
+            const f16x8 x = *reinterpret_cast<const f16x8*>(
+                static_cast<const f16*>(which ? p.v_new : p.k_new) + ((int64_t)b * Hkv + kvh) * DW + 8 * sl);
+            const bool ok = pg >= 0 && pg < p.kv.num_blocks;
+            const int64_t crow = ((int64_t)(ok ? pg : 0) * Hkv + kvh) * BS + (pos % BS);
+            void* cache = const_cast<void*>(which ? p.kv.v : p.kv.k);
+            if constexpr (KV == KV_FP16) {
+                if (ok) *reinterpret_cast<f16x8*>(static_cast<f16*>(cache) + crow * DW + 8 * sl) = x;
+            } else {
+                float s = 1.0f, sigma = 0.0f;
+                if constexpr (KV == KV_E4M3) s = (which ? p.kv.v_scale : p.kv.k_scale)[kvh];
+                const u32x2 w = quantize_slice<KV, 32>(x, s, sigma);   // all 64 lanes take part
+                if (ok) {
+                    *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(cache) + crow * DW + 8 * sl) = w;
+                    if constexpr (KV == KV_INT8)
+                        if (sl == 0) const_cast<float*>(which ? p.kv.v_scale : p.kv.k_scale)[crow] = sigma;
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+    }
+
+    // Q^T operands per half: lane (i, g) holds head i, d = 128h + 64*(kc/2) +
+    // 16g + 8*(kc%2) + [0, 8); heads past the group are zero columns
+    f16x8 qop[2][4];
+    {
+        const f16* q = static_cast<const f16*>(p.q) + (row0 + (i < G ? i : 0)) * DW;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+                qop[h][kc] = i < G ? *reinterpret_cast<const f16x8*>(q + 128 * h + 64 * (kc >> 1) + 16 * g + 8 * (kc & 1))
+                                   : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    float cscale = p.qk_scale_log2;
+    if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
+    float vscale = 1.0f;
+    if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
+    if constexpr (KV == KV_INT8) vscale = 1.0f / 256.0f;
+
+    WaveState2 st;
+    st.m = -__builtin_inff();
+    st.l = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st.acc[h][c] = f32x4{0, 0, 0, 0};
+
+    int dsrc[Dk::kDmaPerPage], kofs[4], vofs[4];
+#pragma unroll
+    for (int q = 0; q < Dk::kDmaPerPage; ++q) dsrc[q] = Dk::dma_src(lane, q);
+    if constexpr (KV == KV_FP16) {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) kofs[kc] = i * (2 * D) + 16 * ((8 * (kc >> 1) + 2 * g + (kc & 1)) ^ i);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) vofs[x] = 0;
+    } else {
+        const int sk = Dk::swap02(i);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) kofs[h] = sk * D + 16 * ((4 * (h & 1) + g) ^ Dk::kap(sk));
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int sv = Dk::swap02(4 * g + x);
+            vofs[x] = sv * D + 16 * ((i >> 1) ^ Dk::kap(sv)) + 8 * (i & 1);
+        }
+    }
+    // vector memory operations of one chunk (both halves; INT8 scales once)
+    constexpr int kOps = 2 * Dk::kIssueOps - (KV == KV_INT8 ? 1 : 0);
+
+    const int my_chunks = cw < nchunks ? (nchunks - cw + NW - 1) / NW : 0;
+    for (int seg = 0; seg < my_chunks; seg += 32) {
+        const int segn = min(32, my_chunks - seg);
+        const int tch = cw + (seg + (lane >> 1)) * NW;
+        const int tb = 2 * tch + (lane & 1);
+        const bool tok = lane < 2 * segn && tb < nblk;
+        const int tbl = !tok ? -1 : (seg == 0 ? tbl0 : bt[blk0 + tb]);
+        auto issue = [&](typename Dk::Meta m[2], int bf, int k) __attribute__((always_inline)) {
+            const int ch = cw + (seg + k) * NW;
+            const int pb0 = __builtin_amdgcn_readlane(tbl, 2 * k), pb1 = __builtin_amdgcn_readlane(tbl, 2 * k + 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                Dk::issue(m[h], &s_dma[wave][bf][h][0], &s_scl[KV == KV_INT8 ? wave : 0][bf][0], p, kvh, pb0, pb1,
+                          2 * ch + 1 < nblk, lane, dsrc, 128 * Dk::EB * h, h == 0);
+        };
+        auto consume = [&](typename Dk::Meta m[2], int bf, int k) __attribute__((always_inline)) {
+            Chunk<KV> c[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                Dk::read(c[h], m[h], &s_dma[wave][bf][h][0], &s_scl[KV == KV_INT8 ? wave : 0][bf][0], kofs, vofs, g);
+            process_chunk_d256<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, g);
+        };
+        typename Dk::Meta ma[2], mb[2];
+        issue(ma, 0, 0);
+        for (int k = 0; k < segn; k += 2) {
+            if (k + 1 < segn) {
+                issue(mb, 1, k + 1);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOps) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            consume(ma, 0, k);
+            if (k + 1 >= segn) break;
+            if (k + 2 < segn) {
+                issue(ma, 0, k + 2);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOps) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            consume(mb, 1, k + 1);
+        }
+    }
+    __syncthreads();                                   // the merge below reuses the DMA buffers
+
+    // ---- merge the waves of the workgroup (fixed order) ----
+    float l_run = st.l;
+    l_run += shfl_xor(l_run, 16);
+    l_run += shfl_xor(l_run, 32);
+    constexpr int AST = DW + 4;
+    float* s_m = smem;                                 // [NW][16]
+    float* s_l = smem + NW * 16;                       // [NW][16]
+    float* s_acc = smem + NW * 32;                     // [NW][G][AST]
+    if (g == 0) {
+        s_m[wave * 16 + i] = st.m;
+        s_l[wave * 16 + i] = l_run;
+    }
+    if (i < G) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float* dst = s_acc + ((int64_t)wave * G + i) * AST + 128 * h + 32 * g;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                f32x4 lo = f32x4{st.acc[h][0][r], st.acc[h][1][r], st.acc[h][2][r], st.acc[h][3][r]};
+                f32x4 hi = f32x4{st.acc[h][4][r], st.acc[h][5][r], st.acc[h][6][r], st.acc[h][7][r]};
+                *reinterpret_cast<f32x4*>(dst + 8 * r) = lo;
+                *reinterpret_cast<f32x4*>(dst + 8 * r + 4) = hi;
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * DW; idx += 64 * NW) {
+        const int j = idx / DW, d = idx % DW;
+        float M = -__builtin_inff();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + j]);
+        float Lsum = 0.0f, O = 0.0f;
+        if (M != -__builtin_inff()) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float wt = fast_exp2(s_m[w * 16 + j] - M);
+                Lsum += s_l[w * 16 + j] * wt;
+                O += s_acc[((int64_t)w * G + j) * AST + d] * wt;
+            }
+        }
+        const bool empty = !(Lsum > 0.0f);
+        p.o_parts[((row0 + j) * nparts + part) * DW + d] = empty ? 0.0f : O * vscale / Lsum;
+        if (d == 0) p.lse_parts[(row0 + j) * nparts + part] = empty ? -__builtin_inff() : (M + __builtin_log2f(Lsum)) * kLn2;
+    }
+}
+
+template <int KV>
+hipError_t launch_d256(const DecodeParams& p, hipStream_t s) {
+    constexpr int NW = 4;
+    static_assert(NW * 2 * 2 * 8192 >= 4 * NW * (32 + 16 * (256 + 4)), "merge space");
+    dim3 grid(p.nparts, p.kv.num_kv_heads, p.num_seqs);
+    hipLaunchKernelGGL((paged_decode256_kernel<KV, NW>), grid, dim3(64 * NW), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.counters) return e;
+    // merged output requested: plc_lse_merge's kernel over the partials
+    return launch_lse_merge(p.o_parts, p.lse_parts, p.num_seqs * p.num_q_heads, p.nparts, 256, p.out, p.lse, s);
+}
+
 template <int KV, int NW, bool MQ>
 hipError_t launch_mq(const DecodeParams& p, hipStream_t s) {
     // the wave-merge and fused-merge buffers live in the kernel's static DMA
@@ -763,6 +1070,15 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s) {
+    if (p.kv.head_dim == 256) {
+        if (p.cu_q_lens) return hipErrorInvalidValue;   // one query token per sequence only
+        switch (p.kv.dtype) {
+        case KV_FP16: return launch_d256<KV_FP16>(p, s);
+        case KV_E4M3: return launch_d256<KV_E4M3>(p, s);
+        case KV_INT8: return launch_d256<KV_INT8>(p, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     // 4 waves for a one-token decode of more than 8 heads per KV head, and
     // for a verification with more than two 16-row groups (enough workgroups
     // to fill the chip; measured faster from 8 drafted tokens at G = 8)

@@ -18,7 +18,7 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int rows, int nparts,
     int D, float* __restrict__ out, float* __restrict__ lse_out) {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
+    const int row = blockIdx.x * kMergeRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= rows) return;
     const float* lp = lse_parts + (int64_t)row * nparts;
     float M = -__builtin_inff();
@@ -31,15 +31,42 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(
     float wsum = 0.0f;
     if (M != -__builtin_inff()) {
         const float* op = o_parts + (int64_t)row * nparts * D;
-        for (int k = 0; k < nparts; ++k) {
-            const float lk = lp[k];
+        // parts in index order; eight parts' loads are issued before any of
+        // them is used, so a row costs about nparts / 8 round trips
+        auto add = [&](float lk, const float ov[VPL]) __attribute__((always_inline)) {
             const float w = (lk == -__builtin_inff()) ? 0.0f : fast_exp2((lk - M) * kLog2e);
             wsum += w;
 #pragma unroll
+            for (int v = 0; v < VPL; ++v) acc[v] += w * ov[v];
+        };
+        int k = 0;
+        for (; k + 8 <= nparts; k += 8) {
+            float lk[8], ov[8][VPL];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                lk[u] = lp[k + u];
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) {
+                    const int d = lane + 64 * v;
+                    ov[u][v] = d < D ? op[(int64_t)(k + u) * D + d] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) pin(ov[u][v]);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) add(lk[u], ov[u]);
+        }
+        for (; k < nparts; ++k) {
+            float ov[VPL];
+#pragma unroll
             for (int v = 0; v < VPL; ++v) {
                 const int d = lane + 64 * v;
-                if (d < D) acc[v] += w * op[(int64_t)k * D + d];
+                ov[v] = d < D ? op[(int64_t)k * D + d] : 0.0f;
             }
+            add(lp[k], ov);
         }
     }
     const bool empty = !(wsum > 0.0f);
@@ -53,20 +80,21 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(
 
 // ------------------------------------------------------------------ append
 //
-// Sixteen lanes per (token, KV head, K-or-V) row of 128 fp16 values, eight
-// values per lane (one 16-byte load).  E4M3 divides by the head's scale in
+// D / 8 lanes (16 for head dim 128, 32 for 256) per (token, KV head, K-or-V)
+// row of D fp16 values, eight values per lane (one 16-byte load).  E4M3 divides by the head's scale in
 // IEEE fp32 and rounds to nearest-even; INT8 takes the row's absolute maximum
-// across the sixteen lanes first (ReVolta README, "INT8 KV": scales per token
+// across the row's lanes first (ReVolta README, "INT8 KV": scales per token
 // and head at run time).
 constexpr int kAppendThreads = 256;
 
-template <int KV>
+template <int KV, int D>
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams p) {
-    constexpr int D = 128, BS = 16;
+    constexpr int BS = 16, LPR = D / 8, LSH = (D == 256) ? 5 : 4;
+    static_assert(LPR == 1 << LSH, "lanes per row");
     const int64_t gid = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
     const int Hkv = p.kv.num_kv_heads;
-    const int64_t row = gid >> 4;                 // (token, head, kv) row
-    const int part = (int)(gid & 15);             // 8-value slice of the row
+    const int64_t row = gid >> LSH;               // (token, head, kv) row
+    const int part = (int)(gid & (LPR - 1));      // 8-value slice of the row
     const int64_t nrows = (int64_t)p.total_new_tokens * Hkv * 2;
     const bool live = row < nrows;
     const int64_t r = live ? row : 0;
@@ -99,7 +127,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
     } else {
         float s = 1.0f, sigma = 0.0f;
         if constexpr (KV == KV_E4M3) s = (which ? p.kv.v_scale : p.kv.k_scale)[h];
-        const u32x2 w = quantize_slice<KV>(x, s, sigma);
+        const u32x2 w = quantize_slice<KV, LPR>(x, s, sigma);
         if (ok) {
             *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(const_cast<void*>(
                 which ? p.kv.v : p.kv.k)) + crow * D + 8 * part) = w;
@@ -139,17 +167,26 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_
     return hipGetLastError();
 }
 
-hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {
-    const int64_t threads = (int64_t)p.total_new_tokens * p.kv.num_kv_heads * 2 * 16;
+template <int D>
+hipError_t launch_kv_append_d(const AppendParams& p, hipStream_t s) {
+    const int64_t threads = (int64_t)p.total_new_tokens * p.kv.num_kv_heads * 2 * (D / 8);
     if (threads == 0) return hipSuccess;
     dim3 grid((unsigned)((threads + kAppendThreads - 1) / kAppendThreads));
     switch (p.kv.dtype) {
-    case KV_FP16: hipLaunchKernelGGL(kv_append_kernel<KV_FP16>, grid, dim3(kAppendThreads), 0, s, p); break;
-    case KV_E4M3: hipLaunchKernelGGL(kv_append_kernel<KV_E4M3>, grid, dim3(kAppendThreads), 0, s, p); break;
-    case KV_INT8: hipLaunchKernelGGL(kv_append_kernel<KV_INT8>, grid, dim3(kAppendThreads), 0, s, p); break;
+    case KV_FP16: hipLaunchKernelGGL((kv_append_kernel<KV_FP16, D>), grid, dim3(kAppendThreads), 0, s, p); break;
+    case KV_E4M3: hipLaunchKernelGGL((kv_append_kernel<KV_E4M3, D>), grid, dim3(kAppendThreads), 0, s, p); break;
+    case KV_INT8: hipLaunchKernelGGL((kv_append_kernel<KV_INT8, D>), grid, dim3(kAppendThreads), 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {
+    switch (p.kv.head_dim) {
+    case 128: return launch_kv_append_d<128>(p, s);
+    case 256: return launch_kv_append_d<256>(p, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_debug_e4m3(const uint8_t* codes, uint16_t* out, int32_t n, hipStream_t s) {

@@ -113,7 +113,7 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
 // so all 16 lanes must call), codes = clamp(rint(x / sigma), -127, 127), an
 // all-zero row giving sigma 0 and zero codes.  Returns the 8 codes, low byte
 // first; sigma is written for INT8.
-template <int KV>
+template <int KV, int LPR = 16>
 __device__ __forceinline__ u32x2 quantize_slice(f16x8 x, float s, float& sigma);
 
 // ------------------------------------------------------------------ MFMA
@@ -141,7 +141,9 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int KV>
+// One lane's eight values of a K or V row held by LPR consecutive lanes (the
+// row has 8 * LPR values; INT8 reduces its maximum over those lanes).
+template <int KV, int LPR>
 __device__ __forceinline__ u32x2 quantize_slice(f16x8 x, float s, float& sigma) {
     uint32_t w[2] = {0, 0};
     if constexpr (KV == KV_E4M3) {
@@ -152,7 +154,7 @@ __device__ __forceinline__ u32x2 quantize_slice(f16x8 x, float s, float& sigma) 
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = fmaxf(m, __builtin_fabsf((float)x[e]));
 #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor(m, off));
+        for (int off = LPR / 2; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor(m, off));
         sigma = m / 127.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {

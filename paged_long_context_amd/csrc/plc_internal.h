@@ -14,6 +14,7 @@ struct KvView {
     const float* v_scale;
     int32_t num_blocks;
     int32_t num_kv_heads;
+    int32_t head_dim;       // 128, or 256 (KV append and one-token decode only)
     int32_t dtype;
 };
 

@@ -1,0 +1,135 @@
+"""GPU: head dim 256 (Split-D) one-token decode and KV append against the oracle.
+
+The group sizes include six query heads per KV head, the packing the pages
+describe for their D256 attention."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from tests import cases
+from tests.gpu_util import assert_close, dev, device_cache, host, sm_scale
+
+pytestmark = pytest.mark.gpu
+
+SM = sm_scale(256)
+LENGTHS = [1, 15, 16, 17, 33, 100, 2047, 2048, 2049, 5000]
+
+
+@pytest.fixture(scope="module")
+def plc():
+    import paged_long_context_amd as m
+    return m
+
+
+def spec(ctx, hq=12, hkv=2, seed=601, **kw):
+    return cases.spec(ctx, [1] * len(ctx), hq=hq, hkv=hkv, d=256, seed=seed, **kw)
+
+
+def run_decode(plc, w, dtype, partition=0, cache=None, bt=None):
+    if cache is None:
+        cache, bt = device_cache(plc, w, dtype)
+    o, l = plc.attn_decode_paged(dev(w.q), cache, bt, dev(w.context_lens), int(w.context_lens.max()),
+                                 partition, SM)
+    torch.cuda.synchronize()
+    return host(o), host(l)
+
+
+def oracle_decode(w, dtype, rows=None):
+    return cases.oracle_attention(w, cases.oracle_cache(w, dtype), SM, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+def test_d256_append_codes_match_oracle(plc, dtype):
+    w = synthetic.generate(spec([37, 16, 100], seed=602))
+    cache, _ = device_cache(plc, w, dtype)
+    torch.cuda.synchronize()
+    ref = cases.oracle_cache(w, dtype)
+    assert np.array_equal(host(cache.k).view(np.uint8), ref.k.view(np.uint8))
+    assert np.array_equal(host(cache.v).view(np.uint8), ref.v.view(np.uint8))
+    if dtype == "int8":
+        ks, vs = ref.scales()
+        assert np.array_equal(host(cache.k_scale), ks, equal_nan=True)
+        assert np.array_equal(host(cache.v_scale), vs, equal_nan=True)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+@pytest.mark.parametrize("partition", [0, 16, 512, 2048])
+def test_d256_decode_lengths(plc, dtype, partition):
+    w = synthetic.generate(spec(LENGTHS, seed=603))
+    o, l = run_decode(plc, w, dtype, partition)
+    ro, rl = oracle_decode(w, dtype)
+    assert_close(o, l, ro, rl, what="d256 decode %s P=%d" % (dtype, partition))
+
+
+@pytest.mark.parametrize("hq,hkv", [(6, 1), (8, 1), (16, 1), (4, 4), (24, 4), (3, 1)])
+@pytest.mark.parametrize("dtype", ["e4m3", "int8"])
+def test_d256_group_sizes(plc, hq, hkv, dtype):
+    w = synthetic.generate(spec([700, 33, 4096], hq=hq, hkv=hkv, seed=604))
+    o, l = run_decode(plc, w, dtype, 512)
+    ro, rl = oracle_decode(w, dtype)
+    assert_close(o, l, ro, rl, what="d256 G=%d %s" % (hq // hkv, dtype))
+
+
+def test_d256_partials_then_merge_equals_decode(plc):
+    w = synthetic.generate(spec([3000, 900, 17], seed=605))
+    cache, bt = device_cache(plc, w, "e4m3")
+    o1, l1 = run_decode(plc, w, "e4m3", 512, cache, bt)
+    op, lp = plc.attn_decode_partials(dev(w.q), cache, bt, dev(w.context_lens), 3000, 512, SM)
+    o2, l2 = plc.lse_merge(op, lp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o2).reshape(o1.shape), o1)
+    assert np.array_equal(host(l2).reshape(l1.shape), l1)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+def test_d256_decode_append_equals_append_then_decode(plc, dtype):
+    lengths = [1, 17, 2048, 2049, 4096, 33]
+    w = synthetic.generate(spec(lengths, seed=606))
+    ca, bt = device_cache(plc, w, dtype, upto="prefix")
+    kn, vn = w.new_kv()
+    plc.kv_append_quant(ca, dev(kn), dev(vn), bt, dev(w.cu_q_lens), dev(w.start_pos))
+    oa, la = plc.attn_decode_paged(dev(w.q), ca, bt, dev(w.context_lens), 4096, 2048, SM)
+    cb, bt2 = device_cache(plc, w, dtype, upto="prefix")
+    ob, lb = plc.attn_decode_append(dev(w.q), dev(kn), dev(vn), cb, bt2, dev(w.context_lens), 4096,
+                                    2048, SM)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ca.k).view(np.uint8), host(cb.k).view(np.uint8))
+    assert np.array_equal(host(ca.v).view(np.uint8), host(cb.v).view(np.uint8))
+    if dtype == "int8":
+        assert np.array_equal(host(ca.k_scale), host(cb.k_scale), equal_nan=True)
+        assert np.array_equal(host(ca.v_scale), host(cb.v_scale), equal_nan=True)
+    assert np.array_equal(host(oa), host(ob)) and np.array_equal(host(la), host(lb))
+    ro, rl = oracle_decode(w, dtype)
+    assert_close(host(ob), host(lb), ro, rl, what="d256 decode_append %s" % dtype)
+
+
+def test_d256_overflowing_logits_and_poison(plc):
+    w = synthetic.generate(spec([3000, 40, 5], seed=607, q_scale=900.0, v_dist="uniform"))
+    for dtype in ["fp16", "e4m3", "int8"]:
+        o, l = run_decode(plc, w, dtype, 1024)
+        ro, rl = oracle_decode(w, dtype)
+        assert np.abs(rl).max() > 1000
+        assert_close(o, l, ro, rl, what="d256 overflow %s" % dtype)
+
+
+def test_d256_is_deterministic_and_placement_independent(plc):
+    w = synthetic.generate(spec([5000, 1234], seed=608))
+    cache, bt = device_cache(plc, w, "e4m3")
+    o1, l1 = run_decode(plc, w, "e4m3", 1024, cache, bt)
+    o2, l2 = run_decode(plc, w, "e4m3", 1024, cache, bt)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    perm = np.random.default_rng(6).permutation(w.num_blocks).astype(np.int32)
+    bt2 = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    w2 = synthetic.Workload(**{**w.__dict__, "block_tables": bt2})
+    o3, l3 = run_decode(plc, w2, "e4m3", 1024)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+
+
+def test_d256_full_decode_shape(plc):
+    # 8 sequences x 32,768-token context, 12 q / 2 kv heads (groups of six),
+    # head dim 256, E4M3, partitions of 2,048: every row against the oracle
+    w = synthetic.generate(spec([32768] * 8, seed=609))
+    o, l = run_decode(plc, w, "e4m3", 2048)
+    ro, rl = oracle_decode(w, "e4m3")
+    assert_close(o, l, ro, rl, what="d256 8x32768 G=6")

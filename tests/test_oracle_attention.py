@@ -26,6 +26,9 @@ DTYPES = ["fp16", "e4m3", "int8"]
     ([50, 33], [1, 20], 8, 1, 128),
     ([19], [19], 8, 8, 16),
     ([300], [40], 8, 1, 128),
+    # head dim 256 with a group of six query heads per KV head
+    ([40, 17], [1, 1], 12, 2, 256),
+    ([70], [6], 6, 1, 256),
 ])
 def test_paged_oracle_matches_dense_sdpa(dtype, shape):
     ctx, ql, hq, hkv, d = shape
