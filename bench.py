@@ -61,6 +61,8 @@ def parse():
                     help="time only the headline step (no per-part graphs), e.g. under a profiler")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill workload (for profiling)")
+    ap.add_argument("--d256-only", action="store_true",
+                    help="only the head dim 256 decode workload")
     ap.add_argument("--verify-only", action="store_true",
                     help="run only the verification-decode workload (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -209,6 +211,32 @@ def bench_window(plc, synthetic, specs, K, window=2048):
     res["workload"] = base.description + "; the same blocks at 32,768-token contexts; eight " \
         "rotated cache copies (the windows' 3 MB per call stay cache-resident, so these are " \
         "latency figures, not HBM-bound ones)"
+    return res
+
+
+def bench_d256(plc, synthetic, specs, K):
+    """Head dim 256 decode step (append + partitions + merge) at the decode
+    batch's shape with groups of six query heads, for each KV dtype."""
+    log("generating d256 (8 x 32768, 12 q / 2 kv, head dim 256)")
+    w = synthetic.generate(specs["d256"])
+    res = {"workload": specs["d256"].description}
+    for dt in ["fp16", "e4m3", "int8"]:
+        # rotated copies: 268 MB (8-bit) / 537 MB (fp16) each, over twice the Infinity Cache
+        c = DecodeCase(plc, w, dt, w.spec.partition_tokens, copies=2 if dt == "fp16" else 4)
+        for i in range(3):
+            c.step(i)
+        n = max(5, min(50, K // 4))
+        sw, se = graph_time(c.step, n, reps=2)
+        _, ke = graph_time(c.partials, n, reps=2)
+        sb = decode_bytes(w, dt) + append_bytes(w, dt)
+        kb = decode_bytes(w, dt, with_outputs=False)
+        res[dt] = {"gbs": round(sb / sw / 1e9, 1), "unit": "GB/s", "us_per_step": round(sw * 1e6, 2),
+                   "step_bytes": sb, "frac_of_hbm_peak": round(sb / sw / 1e9 / HBM_PEAK_GBS, 4),
+                   "partitions_kernel_us": round(ke * 1e6, 2),
+                   "partitions_kernel_gbs": round(kb / ke / 1e9, 1)}
+        log("d256 %s: step %.1f us = %.0f GB/s; partitions %.1f us" % (dt, sw * 1e6, sb / sw / 1e9, ke * 1e6))
+        del c
+        torch.cuda.empty_cache()
     return res
 
 
@@ -459,6 +487,9 @@ def main():
     if args.prefill_only:
         print(json.dumps({"c3_prefill": bench_prefill(plc, synthetic, specs, K)}), flush=True)
         return
+    if args.d256_only:
+        print(json.dumps({"d256_decode": bench_d256(plc, synthetic, specs, K)}), flush=True)
+        return
     if args.verify_only:
         print(json.dumps({"verify_e4m3": bench_verify(plc, synthetic, specs, K),
                           "draft_window_e4m3": bench_window(plc, synthetic, specs, K)}), flush=True)
@@ -554,6 +585,7 @@ def main():
                 torch.cuda.empty_cache()
         extra["verify_e4m3"] = bench_verify(plc, synthetic, specs, K)
         extra["draft_window_e4m3"] = bench_window(plc, synthetic, specs, K)
+        extra["d256_decode"] = bench_d256(plc, synthetic, specs, K)
         result["other_workloads"] = extra
 
     if not args.no_cpu:

@@ -256,6 +256,13 @@ def named_specs() -> Dict[str, Spec]:
         name="draft", context_lens=[524288] * 2 + [262144] * 4, q_lens=[8] * 6, seed=BASE_SEED + 7,
         description="draft attention: 2 x 524,288 + 4 x 262,144 context, 8-token blocks, "
                     "2,048-token sliding window, 8 q / 1 kv, E4M3")
+    # and the wide head: head dim 256 with six query heads per KV head, at the
+    # decode batch's shape
+    s["d256"] = Spec(
+        name="d256", context_lens=[32768] * 8, q_lens=[1] * 8, num_q_heads=12, num_kv_heads=2,
+        head_dim=256, partition_tokens=2048, kv_dtypes=(KV_FP16, KV_E4M3, KV_INT8), seed=BASE_SEED + 8,
+        description="head dim 256 decode: 8 x 32,768 context, 12 q / 2 kv heads (groups of six), "
+                    "FP16 / E4M3 / INT8 KV, partitions of 2,048")
     return s
 
 

@@ -126,10 +126,16 @@ def test_d256_is_deterministic_and_placement_independent(plc):
     assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
 
 
-def test_d256_full_decode_shape(plc):
-    # 8 sequences x 32,768-token context, 12 q / 2 kv heads (groups of six),
-    # head dim 256, E4M3, partitions of 2,048: every row against the oracle
-    w = synthetic.generate(spec([32768] * 8, seed=609))
-    o, l = run_decode(plc, w, "e4m3", 2048)
-    ro, rl = oracle_decode(w, "e4m3")
-    assert_close(o, l, ro, rl, what="d256 8x32768 G=6")
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+def test_d256_full_decode_step(plc, dtype):
+    # the bench workload (8 x 32,768 context, 12 q / 2 kv heads, head dim 256,
+    # partitions of 2,048) in the bench's call: append each sequence's step
+    # token and attend, one call; every row against the oracle
+    w = synthetic.generate(synthetic.named_specs()["d256"])
+    cache, bt = device_cache(plc, w, dtype, upto="prefix")
+    kn, vn = w.new_kv()
+    o, l = plc.attn_decode_append(dev(w.q), dev(kn), dev(vn), cache, bt, dev(w.context_lens), 32768,
+                                  2048, SM)
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(w, dtype)
+    assert_close(host(o), host(l), ro, rl, what="d256 step 8x32768 G=6 %s" % dtype)
