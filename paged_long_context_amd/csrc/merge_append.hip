@@ -8,74 +8,62 @@ namespace {
 
 // ------------------------------------------------------------------ merge
 //
-// One wave per row.  Parts are visited in index order (1Cat-vLLM README,
-// Layer 2 "Split-KV3": the fp32 partial states of the partitions are combined),
-// so the result does not depend on how the rows are scheduled.
-constexpr int kMergeRowsPerBlock = 4;
+// One wave per (row, 64-column slice); lane l owns column 64 * slice + l.
+// Parts are visited in index order (1Cat-vLLM README, Layer 2 "Split-KV3": the
+// fp32 partial states of the partitions are combined), so the result does not
+// depend on how the rows are scheduled.  Lane k of a wave computes part k's
+// weight and readlane hands it to every lane; sixteen parts' values are loaded
+// before any is used, so a row of up to sixteen parts costs one round trip.
+constexpr int kMergeWavesPerBlock = 4;
 
-template <int VPL>   // values per lane: head_dim <= 64 * VPL
-__global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(
+__global__ __launch_bounds__(64 * kMergeWavesPerBlock) void lse_merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int rows, int nparts,
     int D, float* __restrict__ out, float* __restrict__ lse_out) {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * kMergeRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nslice = (D + 63) / 64;
+    const int wv = blockIdx.x * kMergeWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row = wv / nslice, slice = wv - row * nslice;
     if (row >= rows) return;
+    const int d = 64 * slice + lane;
+    const bool dv = d < D;
     const float* lp = lse_parts + (int64_t)row * nparts;
     float M = -__builtin_inff();
     for (int k = lane; k < nparts; k += 64) M = fmaxf(M, lp[k]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
-    float acc[VPL];
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) acc[v] = 0.0f;
-    float wsum = 0.0f;
+    float acc = 0.0f, wsum = 0.0f;
     if (M != -__builtin_inff()) {
-        const float* op = o_parts + (int64_t)row * nparts * D;
-        // parts in index order; eight parts' loads are issued before any of
-        // them is used, so a row costs about nparts / 8 round trips
-        auto add = [&](float lk, const float ov[VPL]) __attribute__((always_inline)) {
-            const float w = (lk == -__builtin_inff()) ? 0.0f : fast_exp2((lk - M) * kLog2e);
-            wsum += w;
+        const float* op = o_parts + (int64_t)row * nparts * D + (dv ? d : 0);
+        for (int kb = 0; kb < nparts; kb += 64) {
+            const int kn = min(64, nparts - kb);
+            const float lk = lane < kn ? lp[kb + lane] : -__builtin_inff();
+            const float wl = (lk == -__builtin_inff()) ? 0.0f : fast_exp2((lk - M) * kLog2e);
+            int k = 0;
+            for (; k + 16 <= kn; k += 16) {
+                float ov[16];
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) acc[v] += w * ov[v];
-        };
-        int k = 0;
-        for (; k + 8 <= nparts; k += 8) {
-            float lk[8], ov[8][VPL];
+                for (int u = 0; u < 16; ++u) ov[u] = dv ? op[(int64_t)(kb + k + u) * D] : 0.0f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                lk[u] = lp[k + u];
+                for (int u = 0; u < 16; ++u) pin(ov[u]);
 #pragma unroll
-                for (int v = 0; v < VPL; ++v) {
-                    const int d = lane + 64 * v;
-                    ov[u][v] = d < D ? op[(int64_t)(k + u) * D + d] : 0.0f;
+                for (int u = 0; u < 16; ++u) {
+                    const float w = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k + u));
+                    wsum += w;
+                    acc += w * ov[u];
                 }
             }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-#pragma unroll
-                for (int v = 0; v < VPL; ++v) pin(ov[u][v]);
+            for (; k < kn; ++k) {
+                const float ov = dv ? op[(int64_t)(kb + k) * D] : 0.0f;
+                const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k));
+                wsum += w;
+                acc += w * ov;
             }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) add(lk[u], ov[u]);
-        }
-        for (; k < nparts; ++k) {
-            float ov[VPL];
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) {
-                const int d = lane + 64 * v;
-                ov[v] = d < D ? op[(int64_t)k * D + d] : 0.0f;
-            }
-            add(lp[k], ov);
         }
     }
     const bool empty = !(wsum > 0.0f);
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-        const int d = lane + 64 * v;
-        if (d < D) out[(int64_t)row * D + d] = empty ? 0.0f : acc[v] / wsum;
-    }
-    if (lane == 0) lse_out[row] = empty ? -__builtin_inff() : M + __builtin_logf(wsum);
+    if (dv) out[(int64_t)row * D + d] = empty ? 0.0f : acc / wsum;
+    if (slice == 0 && lane == 0) lse_out[row] = empty ? -__builtin_inff() : M + __builtin_logf(wsum);
 }
 
 // ------------------------------------------------------------------ append
@@ -150,20 +138,10 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_
                             int32_t nparts, int32_t head_dim, float* out, float* lse_out,
                             hipStream_t s) {
     if (rows == 0) return hipSuccess;
-    dim3 grid((rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock);
-    dim3 block(64 * kMergeRowsPerBlock);
-    if (head_dim <= 64)
-        hipLaunchKernelGGL(lse_merge_kernel<1>, grid, block, 0, s, o_parts, lse_parts, rows, nparts,
-                           head_dim, out, lse_out);
-    else if (head_dim <= 128)
-        hipLaunchKernelGGL(lse_merge_kernel<2>, grid, block, 0, s, o_parts, lse_parts, rows, nparts,
-                           head_dim, out, lse_out);
-    else if (head_dim <= 256)
-        hipLaunchKernelGGL(lse_merge_kernel<4>, grid, block, 0, s, o_parts, lse_parts, rows, nparts,
-                           head_dim, out, lse_out);
-    else
-        hipLaunchKernelGGL(lse_merge_kernel<8>, grid, block, 0, s, o_parts, lse_parts, rows, nparts,
-                           head_dim, out, lse_out);
+    const int64_t waves = (int64_t)rows * ((head_dim + 63) / 64);
+    dim3 grid((unsigned)((waves + kMergeWavesPerBlock - 1) / kMergeWavesPerBlock));
+    hipLaunchKernelGGL(lse_merge_kernel, grid, dim3(64 * kMergeWavesPerBlock), 0, s, o_parts, lse_parts, rows,
+                       nparts, head_dim, out, lse_out);
     return hipGetLastError();
 }
 
