@@ -32,11 +32,12 @@
  *  - head_dim 256 (1Cat-vLLM README, Layer 2 "D256 Split-D": the head is
  *    processed as two 128-wide halves; "GQA Multi-Head Packing": six query
  *    heads per KV head) is taken by plc_kv_append_quant,
- *    plc_attn_decode_partials, plc_attn_decode_paged and
- *    plc_attn_decode_append, with any group size G from 1 to 16.  There the
- *    decode writes partials and merges them in a second kernel (the one of
- *    plc_lse_merge), so the workspace counters are unused.  The other entry
- *    points refuse head_dim 256 with PLC_ERR_UNSUPPORTED.
+ *    plc_attn_decode_partials, plc_attn_decode_paged, plc_attn_decode_append,
+ *    plc_attn_verify_paged and plc_attn_window_paged, with any group size G
+ *    from 1 to 16.  There the attention writes partials and merges them in a
+ *    second kernel (the one of plc_lse_merge), so the workspace counters are
+ *    unused.  plc_attn_prefill_paged refuses head_dim 256 with
+ *    PLC_ERR_UNSUPPORTED.
  */
 #ifndef PLC_H
 #define PLC_H

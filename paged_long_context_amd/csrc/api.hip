@@ -169,6 +169,7 @@ int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
     p.max_q_len = 1;
     p.ncg = 1;
     p.window = 0;
+    p.total_q_tokens = num_seqs;
     return PLC_OK;
 }
 
@@ -379,7 +380,6 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
                           void* workspace, size_t workspace_bytes, void* stream) {
     int rc;
     if ((rc = check_cache(kv))) return rc;
-    if ((rc = check_narrow(kv, "verification / window attention"))) return rc;
     if ((rc = check_heads(num_q_heads, kv))) return rc;
     if ((rc = check_lengths(num_seqs, max_blocks, max_context_len, kv->block_size))) return rc;
     if (total_q_tokens < 0)
@@ -436,6 +436,7 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     p.max_q_len = max_q_len;
     p.ncg = ncg;
     p.window = window_tokens;
+    p.total_q_tokens = total_q_tokens;
     return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)),
                       window_tokens > 0 ? "window launch" : "verify launch");
 }

@@ -762,17 +762,21 @@ struct WaveState2 {
     f32x4 acc[2][8];               // half h: O^T[d = 128h + 32g + 8r + c][head i] in acc[h][c][r]
 };
 
-template <int KV, int NW>
+// lim1 / lo1: the lane's row scores keys in [lo1, lim1) (lim1 = tok1 and no
+// lower bound for a one-token decode); V is zeroed only for keys outside the
+// partition or on invalid pages, since every row shares the V operands.
+template <int KV, int NW, bool LO>
 __device__ __forceinline__ void process_chunk_d256(WaveState2& st, Chunk<KV> cur[2], const f16x8 qop[2][4],
-                                                   float cscale, int ctok, int tok1, int g) {
+                                                   float cscale, int ctok, int tok1, int lo1, int lim1, int g) {
     using Dk = Decode<KV, NW, 256>;
-    bool ok[8];
-    token_ok<false>(ok, ctok, 0, tok1, cur[0].valid_blk, g);
+    bool ok[8], vok[8];
+    token_ok<LO>(ok, ctok, lo1, lim1, cur[0].valid_blk, g);
+    token_ok<false>(vok, ctok, 0, tok1, cur[0].valid_blk, g);
     const bool partial = (ctok + 32 > tok1) || (cur[0].valid_blk != 3);
     if constexpr (KV != KV_FP16)
         if (partial) {
-            Dk::mask_v(cur[0], ok);                 // one-token decode: key validity is the mask
-            Dk::mask_v(cur[1], ok);
+            Dk::mask_v(cur[0], vok);
+            Dk::mask_v(cur[1], vok);
         }
     float x[8];
 #pragma unroll
@@ -829,14 +833,16 @@ __device__ __forceinline__ void process_chunk_d256(WaveState2& st, Chunk<KV> cur
 #pragma unroll
                 for (int c = 0; c < 8; ++c)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) vt[c][e] = ok[e] ? vt[c][e] : (f16)0.0f;
+                    for (int e = 0; e < 8; ++e) vt[c][e] = vok[e] ? vt[c][e] : (f16)0.0f;
             }
 #pragma unroll
         for (int c = 0; c < 8; ++c) st.acc[h][c] = mfma16(vt[c], pop, st.acc[h][c]);
     }
 }
 
-template <int KV, int NW>
+// MQ: several query tokens per sequence (verification, sliding window), the
+// rows of a (sequence, KV head) in groups of 16 as in the 128-wide kernel.
+template <int KV, int NW, bool MQ>
 __global__ __launch_bounds__(64 * NW) void paged_decode256_kernel(DecodeParams p) {
     using Dk = Decode<KV, NW, 256>;
     constexpr int DW = 256;
@@ -844,30 +850,59 @@ __global__ __launch_bounds__(64 * NW) void paged_decode256_kernel(DecodeParams p
     __shared__ __attribute__((aligned(16))) uint8_t s_dma[NW][2][2][8192];
     __shared__ __attribute__((aligned(16))) f32x4 s_scl[KV == KV_INT8 ? NW : 1][2][KV == KV_INT8 ? 64 : 1];
     float* smem = reinterpret_cast<float*>(&s_dma[0][0][0][0]);
-    const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int part = blockIdx.x, b = blockIdx.z;
+    const int kvh = MQ ? (int)blockIdx.y / p.ncg : (int)blockIdx.y;
+    const int cg = MQ ? (int)blockIdx.y - kvh * p.ncg : 0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int cw = NW - 1 - wave;
     const int g = lane >> 4, i = lane & 15;
     const int Hq = p.num_q_heads, Hkv = p.kv.num_kv_heads, G = Hq / Hkv;
     const int P = p.partition_tokens;
-    const int blk0 = part * (P / BS);
+    int blk0 = part * (P / BS);
     const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
     const int tb0 = 2 * (cw + (lane >> 1) * NW) + (lane & 1);
-    const int tbl0 = bt[min(blk0 + tb0, p.max_blocks - 1)];
+    int tbl0 = MQ ? 0 : bt[min(blk0 + tb0, p.max_blocks - 1)];
     const int L = max(0, min(p.context_lens[b], p.max_context_len));
     const int nparts = p.nparts;
-    const int nparts_b = (L + P - 1) / P;
-    const int64_t row0 = (int64_t)b * Hq + (int64_t)kvh * G;      // the group's first query head's row
+    int n = 1;
+    int64_t qa = b;                                                 // the sequence's first query token
+    if constexpr (MQ) {
+        qa = p.cu_q_lens[b];
+        n = min(max(p.cu_q_lens[b + 1] - p.cu_q_lens[b], 0), p.max_q_len);
+    }
+    const int NC = MQ ? min(16, n * G - 16 * cg) : G;               // rows of this workgroup
+    if (MQ && NC <= 0) return;
+    // row of column c: r = 16 cg + c is query token qa + r / G, head kvh G + r % G
+    auto row_of = [&](int c) __attribute__((always_inline)) {
+        const int r = 16 * cg + c;
+        return (qa + r / G) * Hq + (int64_t)kvh * G + r % G;
+    };
+    int lo_min = 0, first_part = 0;
+    if constexpr (MQ)
+        if (p.window > 0) {
+            lo_min = max(0, L - n + 1 - p.window);
+            first_part = lo_min / P;
+        }
+    const int nparts_b = (L + P - 1) / P - first_part;
+    int tok0 = (part + first_part) * P;
     if (part >= nparts_b) {                                        // partition past the end
-        for (int idx = tid; idx < G * DW; idx += 64 * NW) {
+        for (int idx = tid; idx < NC * DW; idx += 64 * NW) {
             const int j = idx / DW, d = idx % DW;
-            p.o_parts[((row0 + j) * nparts + part) * DW + d] = 0.0f;
-            if (d == 0) p.lse_parts[(row0 + j) * nparts + part] = -__builtin_inff();
+            const int64_t row = row_of(j);
+            p.o_parts[(row * nparts + part) * DW + d] = 0.0f;
+            if (d == 0) p.lse_parts[row * nparts + part] = -__builtin_inff();
         }
         return;
     }
-    const int tok0 = part * P, tok1 = min(tok0 + P, L);
+    const int tok1 = min(tok0 + P, L);
+    if constexpr (MQ) {
+        // skip the chunks below every row's window, then fetch the first
+        // segment's page ids
+        tok0 += 32 * (max(0, lo_min - tok0) / 32);
+        blk0 = tok0 / BS;
+        tbl0 = bt[min(blk0 + tb0, p.max_blocks - 1)];
+    }
     const int nblk = (tok1 - tok0 + BS - 1) / BS;
     const int nchunks = (nblk + 1) / 2;
 
@@ -901,18 +936,23 @@ __global__ __launch_bounds__(64 * NW) void paged_decode256_kernel(DecodeParams p
         __syncthreads();
     }
 
-    // Q^T operands per half: lane (i, g) holds head i, d = 128h + 64*(kc/2) +
-    // 16g + 8*(kc%2) + [0, 8); heads past the group are zero columns
+    // Q^T operands per half: lane (i, g) holds column i, d = 128h + 64*(kc/2) +
+    // 16g + 8*(kc%2) + [0, 8); columns past the rows are zero.  Its causal
+    // limit: position L - n + j sees keys below L - n + j + 1 (L for a
+    // one-token decode), and with a window none below that minus the window.
     f16x8 qop[2][4];
     {
-        const f16* q = static_cast<const f16*>(p.q) + (row0 + (i < G ? i : 0)) * DW;
+        const f16* q = static_cast<const f16*>(p.q) + row_of(i < NC ? i : 0) * DW;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc)
-                qop[h][kc] = i < G ? *reinterpret_cast<const f16x8*>(q + 128 * h + 64 * (kc >> 1) + 16 * g + 8 * (kc & 1))
-                                   : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                qop[h][kc] = i < NC ? *reinterpret_cast<const f16x8*>(q + 128 * h + 64 * (kc >> 1) + 16 * g + 8 * (kc & 1))
+                                    : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
+    const int lim = i < NC ? L - n + 1 + (16 * cg + i) / G : 0;
+    const int lim1 = MQ ? min(lim, tok1) : tok1;
+    const int lo1 = p.window > 0 ? lim - p.window : 0;
     float cscale = p.qk_scale_log2;
     if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
     float vscale = 1.0f;
@@ -968,7 +1008,8 @@ __global__ __launch_bounds__(64 * NW) void paged_decode256_kernel(DecodeParams p
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 Dk::read(c[h], m[h], &s_dma[wave][bf][h][0], &s_scl[KV == KV_INT8 ? wave : 0][bf][0], kofs, vofs, g);
-            process_chunk_d256<KV, NW>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, g);
+            process_chunk_d256<KV, NW, MQ>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, lo1, lim1,
+                                           g);
         };
         typename Dk::Meta ma[2], mb[2];
         issue(ma, 0, 0);
@@ -999,15 +1040,15 @@ __global__ __launch_bounds__(64 * NW) void paged_decode256_kernel(DecodeParams p
     constexpr int AST = DW + 4;
     float* s_m = smem;                                 // [NW][16]
     float* s_l = smem + NW * 16;                       // [NW][16]
-    float* s_acc = smem + NW * 32;                     // [NW][G][AST]
+    float* s_acc = smem + NW * 32;                     // [NW][NC][AST]
     if (g == 0) {
         s_m[wave * 16 + i] = st.m;
         s_l[wave * 16 + i] = l_run;
     }
-    if (i < G) {
+    if (i < NC) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            float* dst = s_acc + ((int64_t)wave * G + i) * AST + 128 * h + 32 * g;
+            float* dst = s_acc + ((int64_t)wave * NC + i) * AST + 128 * h + 32 * g;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 f32x4 lo = f32x4{st.acc[h][0][r], st.acc[h][1][r], st.acc[h][2][r], st.acc[h][3][r]};
@@ -1018,7 +1059,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode256_kernel(DecodeParams p
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * DW; idx += 64 * NW) {
+    for (int idx = tid; idx < NC * DW; idx += 64 * NW) {
         const int j = idx / DW, d = idx % DW;
         float M = -__builtin_inff();
 #pragma unroll
@@ -1029,12 +1070,13 @@ __global__ __launch_bounds__(64 * NW) void paged_decode256_kernel(DecodeParams p
             for (int w = 0; w < NW; ++w) {
                 const float wt = fast_exp2(s_m[w * 16 + j] - M);
                 Lsum += s_l[w * 16 + j] * wt;
-                O += s_acc[((int64_t)w * G + j) * AST + d] * wt;
+                O += s_acc[((int64_t)w * NC + j) * AST + d] * wt;
             }
         }
         const bool empty = !(Lsum > 0.0f);
-        p.o_parts[((row0 + j) * nparts + part) * DW + d] = empty ? 0.0f : O * vscale / Lsum;
-        if (d == 0) p.lse_parts[(row0 + j) * nparts + part] = empty ? -__builtin_inff() : (M + __builtin_log2f(Lsum)) * kLn2;
+        const int64_t row = row_of(j);
+        p.o_parts[(row * nparts + part) * DW + d] = empty ? 0.0f : O * vscale / Lsum;
+        if (d == 0) p.lse_parts[row * nparts + part] = empty ? -__builtin_inff() : (M + __builtin_log2f(Lsum)) * kLn2;
     }
 }
 
@@ -1042,12 +1084,16 @@ template <int KV>
 hipError_t launch_d256(const DecodeParams& p, hipStream_t s) {
     constexpr int NW = 4;
     static_assert(NW * 2 * 2 * 8192 >= 4 * NW * (32 + 16 * (256 + 4)), "merge space");
-    dim3 grid(p.nparts, p.kv.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((paged_decode256_kernel<KV, NW>), grid, dim3(64 * NW), 0, s, p);
+    dim3 grid(p.nparts, p.kv.num_kv_heads * p.ncg, p.num_seqs);
+    if (p.cu_q_lens)
+        hipLaunchKernelGGL((paged_decode256_kernel<KV, NW, true>), grid, dim3(64 * NW), 0, s, p);
+    else
+        hipLaunchKernelGGL((paged_decode256_kernel<KV, NW, false>), grid, dim3(64 * NW), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.counters) return e;
     // merged output requested: plc_lse_merge's kernel over the partials
-    return launch_lse_merge(p.o_parts, p.lse_parts, p.num_seqs * p.num_q_heads, p.nparts, 256, p.out, p.lse, s);
+    return launch_lse_merge(p.o_parts, p.lse_parts, p.total_q_tokens * p.num_q_heads, p.nparts, 256, p.out,
+                            p.lse, s);
 }
 
 template <int KV, int NW, bool MQ>
@@ -1071,7 +1117,6 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
 
 hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s) {
     if (p.kv.head_dim == 256) {
-        if (p.cu_q_lens) return hipErrorInvalidValue;   // one query token per sequence only
         switch (p.kv.dtype) {
         case KV_FP16: return launch_d256<KV_FP16>(p, s);
         case KV_E4M3: return launch_d256<KV_E4M3>(p, s);

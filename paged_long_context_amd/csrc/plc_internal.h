@@ -55,6 +55,9 @@ struct DecodeParams {
     // pos - window + 1 .. pos, and partition k of a sequence is then the k-th
     // one from the partition holding its first query's first key
     int32_t window;
+    // query tokens in the call (rows = total_q_tokens * num_q_heads): num_seqs
+    // for a one-token decode, cu_q_lens[num_seqs] with cu_q_lens
+    int32_t total_q_tokens;
 };
 
 hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s);

@@ -168,9 +168,9 @@ def test_verify_workspace_size_formula(plc):
 
 
 def test_head_dim_256_entry_points(plc):
-    # head dim 256 is taken by KV append and one-token decode; a group of six
-    # query heads is accepted there, and the other entry points refuse the
-    # width before touching memory
+    # head dim 256 is taken by KV append and the decode family (one token,
+    # verification, window); a group of six query heads is accepted there, and
+    # prefill refuses the width before touching memory
     d = _desc(plc, head_dim=256, hkv=2)
     assert _decode(plc, d, hq=12, ws=None) == -3                      # validation passed up to the workspace
     assert _decode(plc, d, hq=12 * 3) == -2 and "1..16" in _err(plc)  # group of 18
@@ -179,5 +179,5 @@ def test_head_dim_256_entry_points(plc):
     assert L.plc_attn_prefill_paged(0x1, 12, ctypes.byref(d), 0x1, 4, 0x1, 0x1, 1, 10, 10, 64,
                                     0.1, 0x1, 0x1, None) == -2
     assert "head_dim 128 only" in _err(plc)
-    assert _verify(plc, d, hq=12) == -2 and "head_dim 128 only" in _err(plc)
+    assert _verify(plc, d, hq=12, ws=None) == -3                      # validation passed up to the workspace
     assert _decode(plc, _desc(plc, head_dim=192)) == -2 and "head_dim" in _err(plc)

@@ -1,4 +1,5 @@
-"""GPU: head dim 256 (Split-D) one-token decode and KV append against the oracle.
+"""GPU: head dim 256 (Split-D) KV append, one-token decode, verification and
+sliding-window attention against the oracle.
 
 The group sizes include six query heads per KV head, the packing the pages
 describe for their D256 attention."""
@@ -8,7 +9,7 @@ import torch
 
 import synthetic
 from tests import cases
-from tests.gpu_util import assert_close, dev, device_cache, host, sm_scale
+from tests.gpu_util import append_new, assert_close, dev, device_cache, host, sm_scale
 
 pytestmark = pytest.mark.gpu
 
@@ -139,3 +140,59 @@ def test_d256_full_decode_step(plc, dtype):
     torch.cuda.synchronize()
     ro, rl = oracle_decode(w, dtype)
     assert_close(host(o), host(l), ro, rl, what="d256 step 8x32768 G=6 %s" % dtype)
+
+
+def run_mq(plc, w, dtype, window=0, partition=0):
+    """Cache the prefix, append the new tokens, then verify (window 0) or attend
+    through the window."""
+    cache, bt = device_cache(plc, w, dtype, upto="prefix")
+    append_new(plc, cache, w, bt)
+    mq = max(1, int(np.diff(w.cu_q_lens).max()))
+    o, l = plc.attn_window_paged(dev(w.q), cache, bt, dev(w.cu_q_lens), dev(w.context_lens), mq,
+                                 int(w.context_lens.max()), window, partition, SM)
+    torch.cuda.synchronize()
+    return host(o), host(l)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+@pytest.mark.parametrize("n", [2, 4, 7, 16])
+def test_d256_verify(plc, dtype, n):
+    # drafted tokens causal among themselves; rows = n * 6 per KV head, split
+    # into groups of 16 that do not align with tokens
+    ctx = [n, 17, 33, 2047, 2049, 5000]
+    w = synthetic.generate(cases.spec(ctx, [n] * len(ctx), hq=12, hkv=2, d=256, seed=620 + n))
+    for P in [0, 16, 512]:
+        o, l = run_mq(plc, w, dtype, 0, P)
+        ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, dtype), SM)
+        assert_close(o, l, ro, rl, what="d256 verify n=%d %s P=%d" % (n, dtype, P))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+@pytest.mark.parametrize("window", [1, 17, 2048])
+def test_d256_window(plc, dtype, window):
+    ctx = [8, 50, 2048, 4103, 5000]
+    w = synthetic.generate(cases.spec(ctx, [8] * len(ctx), hq=12, hkv=2, d=256, seed=640 + window))
+    for P in [0, 512]:
+        o, l = run_mq(plc, w, dtype, window, P)
+        ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, dtype), SM, window=window)
+        assert_close(o, l, ro, rl, what="d256 window %d %s P=%d" % (window, dtype, P))
+
+
+def test_d256_verify_one_token_equals_decode(plc):
+    w = synthetic.generate(spec([3000, 17, 2049], seed=650))
+    cache, bt = device_cache(plc, w, "e4m3")
+    od, ld = run_decode(plc, w, "e4m3", 512, cache, bt)
+    ov, lv = plc.attn_verify_paged(dev(w.q), cache, bt, dev(w.cu_q_lens), dev(w.context_lens), 1,
+                                   3000, 512, SM)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ov).reshape(od.shape), od) and np.array_equal(host(lv).reshape(ld.shape), ld)
+
+
+def test_d256_verify_ragged_and_group_sizes(plc):
+    for hq, hkv in [(6, 1), (16, 1), (3, 3), (24, 4)]:
+        w = synthetic.generate(cases.spec([700, 3000, 64, 5], [5, 3, 16, 0], hq=hq, hkv=hkv, d=256,
+                                          seed=660 + hq))
+        for dtype in ["e4m3", "int8"]:
+            o, l = run_mq(plc, w, dtype, 0, 512)
+            ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, dtype), SM)
+            assert_close(o, l, ro, rl, what="d256 verify G=%d %s" % (hq // hkv, dtype))
