@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill workload (for profiling)")
     ap.add_argument("--d256-only", action="store_true",
-                    help="only the head dim 256 decode workload")
+                    help="only the head dim 256 workloads (decode, prefill)")
     ap.add_argument("--verify-only", action="store_true",
                     help="run only the verification-decode workload (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -238,6 +238,38 @@ def bench_d256(plc, synthetic, specs, K):
         del c
         torch.cuda.empty_cache()
     return res
+
+
+def bench_d256_prefill(plc, synthetic, specs, K):
+    """Head dim 256 chunked prefill: 8,192 new tokens after 122,880 cached, groups of six."""
+    log("generating d256_prefill (8192 new after 122880 cached, 12 q / 2 kv, head dim 256)")
+    w = synthetic.generate(specs["d256_prefill"])
+    s = w.spec
+    caches, bt = build_cache(plc, w, "e4m3", 1)
+    cache = caches[0]
+    q = to_dev(w.q)
+    cu, ctx = to_dev(w.cu_q_lens), to_dev(w.context_lens)
+    kn, vn = w.new_kv()
+    plc.kv_append_quant(cache, to_dev(kn), to_dev(vn), bt, cu, to_dev(w.start_pos))
+    T = int(w.cu_q_lens[-1])
+    out = torch.empty((T, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, s.num_q_heads), dtype=torch.float32, device="cuda")
+    sm = 1.0 / math.sqrt(s.head_dim)
+
+    def pre(i):
+        plc.attn_prefill_paged(q, cache, bt, cu, ctx, T, int(w.context_lens.max()), sm, out=out, lse=lse)
+    pre(0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all()), "d256 prefill output"
+    pw, pe = graph_time(pre, 3, reps=2)
+    fl = prefill_flops(w)
+    tf = fl / pe / 1e12
+    log("d256 prefill %.1f us, %.1f TFLOP/s" % (pe * 1e6, tf))
+    del caches, cache, q, out, lse
+    torch.cuda.empty_cache()
+    return {"workload": s.description, "tflops": round(tf, 2), "unit": "TFLOP/s",
+            "us_per_call": round(pe * 1e6, 1), "useful_flops": fl,
+            "frac_of_f16_mfma_peak": round(tf / F16_MFMA_PEAK_TFLOPS, 4)}
 
 
 def prefill_flops(w):
@@ -488,7 +520,8 @@ def main():
         print(json.dumps({"c3_prefill": bench_prefill(plc, synthetic, specs, K)}), flush=True)
         return
     if args.d256_only:
-        print(json.dumps({"d256_decode": bench_d256(plc, synthetic, specs, K)}), flush=True)
+        print(json.dumps({"d256_decode": bench_d256(plc, synthetic, specs, K),
+                          "d256_prefill": bench_d256_prefill(plc, synthetic, specs, K)}), flush=True)
         return
     if args.verify_only:
         print(json.dumps({"verify_e4m3": bench_verify(plc, synthetic, specs, K),
@@ -586,6 +619,7 @@ def main():
         extra["verify_e4m3"] = bench_verify(plc, synthetic, specs, K)
         extra["draft_window_e4m3"] = bench_window(plc, synthetic, specs, K)
         extra["d256_decode"] = bench_d256(plc, synthetic, specs, K)
+        extra["d256_prefill"] = bench_d256_prefill(plc, synthetic, specs, K)
         result["other_workloads"] = extra
 
     if not args.no_cpu:

@@ -71,13 +71,6 @@ int check_heads(int32_t num_q_heads, const plc_kv_cache* kv) {
     return PLC_OK;
 }
 
-// Entry points built for head dim 128 only.
-int check_narrow(const plc_kv_cache* kv, const char* what) {
-    if (kv->head_dim != kHeadDim)
-        return fail(PLC_ERR_UNSUPPORTED, "%s is built for head_dim %d only (got %d)", what, kHeadDim,
-                    kv->head_dim);
-    return PLC_OK;
-}
 
 int check_lengths(int32_t num_seqs, int32_t max_blocks, int32_t max_context_len, int32_t block_size) {
     if (num_seqs <= 0) return fail(PLC_ERR_INVALID_ARG, "num_seqs %d must be positive", num_seqs);
@@ -238,7 +231,6 @@ int plc_attn_prefill_paged(const void* q, int32_t num_q_heads, const plc_kv_cach
                            void* stream) {
     int rc;
     if ((rc = check_cache(kv))) return rc;
-    if ((rc = check_narrow(kv, "plc_attn_prefill_paged"))) return rc;
     if ((rc = check_heads(num_q_heads, kv))) return rc;
     if ((rc = check_lengths(num_seqs, max_blocks, max_context_len, kv->block_size))) return rc;
     if (total_q_tokens < 0 || max_q_len < 0)
@@ -266,6 +258,8 @@ int plc_attn_prefill_paged(const void* q, int32_t num_q_heads, const plc_kv_cach
     p.qk_scale_log2 = sm_scale * 1.4426950408889634f;
     p.out = out;
     p.lse = lse;
+    if (kv->head_dim == kHeadDimWide)
+        return hip_status(plc::launch_prefill256(p, static_cast<hipStream_t>(stream)), "prefill launch");
     return hip_status(plc::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 

@@ -97,6 +97,7 @@ struct PrefillParams {
 };
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill256(const PrefillParams& p, hipStream_t s);   // head dim 256
 
 hipError_t launch_debug_e4m3(const uint8_t* codes, uint16_t* out, int32_t n, hipStream_t s);
 

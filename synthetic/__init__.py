@@ -263,6 +263,11 @@ def named_specs() -> Dict[str, Spec]:
         head_dim=256, partition_tokens=2048, kv_dtypes=(KV_FP16, KV_E4M3, KV_INT8), seed=BASE_SEED + 8,
         description="head dim 256 decode: 8 x 32,768 context, 12 q / 2 kv heads (groups of six), "
                     "FP16 / E4M3 / INT8 KV, partitions of 2,048")
+    s["d256_prefill"] = Spec(
+        name="d256_prefill", context_lens=[131072], q_lens=[8192], num_q_heads=12, num_kv_heads=2,
+        head_dim=256, seed=BASE_SEED + 9,
+        description="head dim 256 chunked causal prefill: 8,192 new tokens after a 122,880-token "
+                    "cached prefix, 12 q / 2 kv heads (groups of six), E4M3 KV")
     return s
 
 

@@ -168,16 +168,14 @@ def test_verify_workspace_size_formula(plc):
 
 
 def test_head_dim_256_entry_points(plc):
-    # head dim 256 is taken by KV append and the decode family (one token,
-    # verification, window); a group of six query heads is accepted there, and
-    # prefill refuses the width before touching memory
+    # head dim 256 is taken by every entry point with a group of up to 16
+    # query heads (six here); other widths are refused before touching memory
     d = _desc(plc, head_dim=256, hkv=2)
     assert _decode(plc, d, hq=12, ws=None) == -3                      # validation passed up to the workspace
     assert _decode(plc, d, hq=12 * 3) == -2 and "1..16" in _err(plc)  # group of 18
     assert _decode(plc, _desc(plc, head_dim=128, hkv=2), hq=12) == -2  # G = 6 needs head dim 256
     L = plc.lib()
-    assert L.plc_attn_prefill_paged(0x1, 12, ctypes.byref(d), 0x1, 4, 0x1, 0x1, 1, 10, 10, 64,
-                                    0.1, 0x1, 0x1, None) == -2
-    assert "head_dim 128 only" in _err(plc)
+    assert L.plc_attn_prefill_paged(None, 12, ctypes.byref(d), 0x1, 4, 0x1, 0x1, 1, 10, 10, 64,
+                                    0.1, 0x1, 0x1, None) == -1      # validated up to the null q
     assert _verify(plc, d, hq=12, ws=None) == -3                      # validation passed up to the workspace
     assert _decode(plc, _desc(plc, head_dim=192)) == -2 and "head_dim" in _err(plc)

@@ -196,3 +196,77 @@ def test_d256_verify_ragged_and_group_sizes(plc):
             o, l = run_mq(plc, w, dtype, 0, 512)
             ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, dtype), SM)
             assert_close(o, l, ro, rl, what="d256 verify G=%d %s" % (hq // hkv, dtype))
+
+
+# ---------------------------------------------------------------- prefill
+
+def run_prefill(plc, w, dtype):
+    cache, bt = device_cache(plc, w, dtype, upto="prefix")
+    append_new(plc, cache, w, bt)
+    ql = np.diff(w.cu_q_lens)
+    o, l = plc.attn_prefill_paged(dev(w.q), cache, bt, dev(w.cu_q_lens), dev(w.context_lens),
+                                  max(1, int(ql.max())), int(w.context_lens.max()), SM)
+    torch.cuda.synchronize()
+    return host(o), host(l)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+def test_d256_prefill_from_empty(plc, dtype):
+    w = synthetic.generate(cases.spec([512], [512], hq=12, hkv=2, d=256, seed=670))
+    o, l = run_prefill(plc, w, dtype)
+    ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, dtype), SM)
+    assert_close(o, l, ro, rl, what="d256 prefill 512 %s" % dtype)
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 11, 16, 17, 64, 65])
+@pytest.mark.parametrize("prefix", [0, 1, 31, 32, 33, 2049])
+def test_d256_prefill_short_chunks_after_prefix(plc, chunk, prefix):
+    # row groups of 64 = 10 2/3 positions at six heads: groups cut positions
+    w = synthetic.generate(cases.spec([prefix + chunk], [chunk], hq=6, hkv=1, d=256, seed=671 + chunk))
+    o, l = run_prefill(plc, w, "e4m3")
+    ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, "e4m3"), SM)
+    assert_close(o, l, ro, rl, what="d256 chunk %d prefix %d" % (chunk, prefix))
+
+
+@pytest.mark.parametrize("hq,hkv", [(6, 1), (12, 2), (16, 1), (4, 4), (3, 1)])
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+def test_d256_prefill_group_sizes_and_ragged_batch(plc, hq, hkv, dtype):
+    w = synthetic.generate(cases.spec([300, 77, 1000, 5], [300, 20, 150, 0], hq=hq, hkv=hkv, d=256,
+                                      seed=680))
+    o, l = run_prefill(plc, w, dtype)
+    ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, dtype), SM)
+    assert_close(o, l, ro, rl, what="d256 prefill G=%d %s" % (hq // hkv, dtype))
+
+
+def test_d256_prefill_last_row_matches_decode(plc):
+    # the last row of a prefill agrees with a one-token decode over the same keys
+    w = synthetic.generate(cases.spec([700], [700], hq=12, hkv=2, d=256, seed=690))
+    o, l = run_prefill(plc, w, "e4m3")
+    cache, bt = device_cache(plc, w, "e4m3")
+    q_last = w.q[-1:]
+    od, ld = plc.attn_decode_paged(dev(q_last), cache, bt, dev(w.context_lens), 700, 0, SM)
+    torch.cuda.synchronize()
+    assert np.abs(host(od)[0] - o[-1]).max() <= 2e-3     # both within the parity bar of the oracle
+    ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, "e4m3"), SM)
+    assert_close(o, l, ro, rl, what="d256 prefill 700")
+
+
+def test_d256_prefill_overflowing_logits(plc):
+    w = synthetic.generate(cases.spec([1500], [300], hq=6, hkv=1, d=256, seed=691, q_scale=900.0,
+                                      v_dist="uniform"))
+    for dtype in ["fp16", "e4m3", "int8"]:
+        o, l = run_prefill(plc, w, dtype)
+        ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, dtype), SM)
+        assert_close(o, l, ro, rl, what="d256 prefill overflow %s" % dtype)
+
+
+def test_d256_prefill_full_size_subsample(plc):
+    # the bench workload: 8,192 new tokens after 122,880 cached, 12 q / 2 kv
+    # heads, head dim 256, E4M3, on a seeded subsample of 96 query positions
+    # (first and last 8, tile-edge pairs) x all 12 heads
+    w = synthetic.generate(synthetic.named_specs()["d256_prefill"])
+    o, l = run_prefill(plc, w, "e4m3")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    rows = synthetic.subsample_rows(8192, 12, 96, seed=0xD2, tile=32)
+    ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, "e4m3"), SM, rows=rows)
+    assert_close(o, l, ro, rl, rows=rows, what="d256 prefill 8192 after 122880")
