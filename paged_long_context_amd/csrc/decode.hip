@@ -1128,6 +1128,95 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
 // chunks.  Every wave then runs the split-D chunk step over its own rows with
 // its lanes' causal limits and finally writes normalized rows and LSEs.  No
 // split over keys: a long prompt chunk has enough row groups to fill the chip.
+// The split-D chunk step for RG groups of 16 rows that share the chunk: the K
+// and V operands are converted once and feed every group's MFMAs.
+template <int KV, int RG>
+__device__ __forceinline__ void process_chunk_d256_rg(WaveState2 st[RG], Chunk<KV> cur[2],
+                                                      const f16x8 qop[RG][2][4], float cscale, int ctok,
+                                                      int tok1, const int lim1[RG], int g) {
+    using Dk = Decode<KV, 4, 256>;
+    bool vok[8];
+    token_ok<false>(vok, ctok, 0, tok1, cur[0].valid_blk, g);
+    const bool partial = (ctok + 32 > tok1) || (cur[0].valid_blk != 3);
+    if constexpr (KV != KV_FP16)
+        if (partial) {
+            Dk::mask_v(cur[0], vok);
+            Dk::mask_v(cur[1], vok);
+        }
+    float x[RG][8];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+        f32x4 s[RG];
+#pragma unroll
+        for (int j = 0; j < RG; ++j) s[j] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f16x8 kop[4];
+            Dk::k_operands(cur[h], pg, kop);
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+                for (int j = 0; j < RG; ++j) s[j] = mfma16(kop[kc], qop[j][h][kc], s[j]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float sc = cscale;
+            if constexpr (KV == KV_INT8) sc *= cur[0].ks[pg][r];
+#pragma unroll
+            for (int j = 0; j < RG; ++j) x[j][4 * pg + r] = s[j][r] * sc;
+        }
+    }
+    f16x8 pop[RG];
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+        bool ok[8];
+        token_ok<false>(ok, ctok, 0, lim1[j], cur[0].valid_blk, g);
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[j][e] = ok[e] ? x[j][e] : -__builtin_inff();
+            mx = fmaxf(mx, x[j][e]);
+        }
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float m_new = fmaxf(st[j].m, mx);
+        const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+        const float alpha = fast_exp2(st[j].m - m_use);
+        float psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float pe = fast_exp2(x[j][e] - m_use);
+            psum += pe;
+            if constexpr (KV == KV_INT8) pe *= cur[0].vs[e >> 2][e & 3] * 256.0f;
+            pop[j][e] = (f16)pe;
+        }
+        st[j].l = st[j].l * alpha + psum;
+        st[j].m = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) st[j].acc[h][c] *= alpha;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        f16x8 vt[8];
+        Dk::v_operands(cur[h], vt);
+        if constexpr (KV == KV_FP16)
+            if (partial) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vt[c][e] = vok[e] ? vt[c][e] : (f16)0.0f;
+            }
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int j = 0; j < RG; ++j) st[j].acc[h][c] = mfma16(vt[c], pop[j], st[j].acc[h][c]);
+    }
+}
+
 template <int KV>
 __device__ __forceinline__ void pf256_issue(uint8_t* lbuf, f32x4* sbuf, const PrefillParams& p, int kvh, int pb0,
                                             int pb1, bool has1, int lane, const int src[], int hoff, bool scales,
@@ -1166,9 +1255,10 @@ __device__ __forceinline__ void pf256_issue(uint8_t* lbuf, f32x4* sbuf, const Pr
     (void)scales;
 }
 
-template <int KV>
+template <int KV, int RG>
 __global__ __launch_bounds__(256) void paged_prefill256_kernel(PrefillParams p) {
     constexpr int NW = 4, DW = 256;
+    constexpr int RPW = 16 * RG, RWG = NW * RPW;       // rows per wave, per workgroup
     using Dk = Decode<KV, NW, 256>;
     constexpr int HB = (KV == KV_FP16) ? 16384 : 8192;   // bytes of one half-chunk (K then V)
     // DMA vector memory operations of one half-chunk (INT8 scales not counted:
@@ -1185,27 +1275,38 @@ __global__ __launch_bounds__(256) void paged_prefill256_kernel(PrefillParams p) 
     const int64_t qa = p.cu_q_lens[b];
     const int n = min(max(p.cu_q_lens[b + 1] - p.cu_q_lens[b], 0), min(p.max_q_len, L));
     const int nrows = n * G;
-    if (64 * rg >= nrows) return;                                  // uniform: no rows here
+    if (RWG * rg >= nrows) return;                                 // uniform: no rows here
     const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
-    // this lane's row: r = 64 rg + 16 wave + i is query token r / G, head r % G,
-    // at position L - n + r / G, seeing keys below that plus one
-    const int r = 64 * rg + 16 * wave + i;
-    const bool live = r < nrows;
-    const int64_t row = (qa + (live ? r : 0) / G) * Hq + (int64_t)kvh * G + (live ? r : 0) % G;
-    const int lim = live ? L - n + r / G + 1 : 0;
+    // this lane's rows: r = RWG rg + RPW wave + 16 j + i is query token r / G,
+    // head r % G, at position L - n + r / G, seeing keys below that plus one
+    bool live[RG];
+    int64_t row[RG];
+    int lim[RG];
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+        const int r = RWG * rg + RPW * wave + 16 * j + i;
+        live[j] = r < nrows;
+        row[j] = (qa + (live[j] ? r : 0) / G) * Hq + (int64_t)kvh * G + (live[j] ? r : 0) % G;
+        lim[j] = live[j] ? L - n + r / G + 1 : 0;
+    }
     // keys the workgroup's last row sees: the chunk range of every wave
-    const int kend = L - n + (min(64 * rg + 63, nrows - 1)) / G + 1;
+    const int kend = L - n + (min(RWG * rg + RWG - 1, nrows - 1)) / G + 1;
     const int nch = (kend + 31) / 32;
+    int lim1[RG];
+#pragma unroll
+    for (int j = 0; j < RG; ++j) lim1[j] = min(lim[j], kend);
 
-    f16x8 qop[2][4];
-    {
-        const f16* q = static_cast<const f16*>(p.q) + row * DW;
+    f16x8 qop[RG][2][4];
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+        const f16* q = static_cast<const f16*>(p.q) + row[j] * DW;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc)
-                qop[h][kc] = live ? *reinterpret_cast<const f16x8*>(q + 128 * h + 64 * (kc >> 1) + 16 * g + 8 * (kc & 1))
-                                  : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                qop[j][h][kc] = live[j] ? *reinterpret_cast<const f16x8*>(q + 128 * h + 64 * (kc >> 1) + 16 * g +
+                                                                          8 * (kc & 1))
+                                        : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
     float cscale = p.qk_scale_log2;
     if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
@@ -1213,13 +1314,16 @@ __global__ __launch_bounds__(256) void paged_prefill256_kernel(PrefillParams p) 
     if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
     if constexpr (KV == KV_INT8) vscale = 1.0f / 256.0f;
 
-    WaveState2 st;
-    st.m = -__builtin_inff();
-    st.l = 0.0f;
+    WaveState2 st[RG];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int j = 0; j < RG; ++j) {
+        st[j].m = -__builtin_inff();
+        st[j].l = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) st.acc[h][c] = f32x4{0, 0, 0, 0};
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st[j].acc[h][c] = f32x4{0, 0, 0, 0};
+    }
 
     int dsrc[Dk::kDmaPerPage], kofs[4], vofs[4];
 #pragma unroll
@@ -1281,43 +1385,47 @@ __global__ __launch_bounds__(256) void paged_prefill256_kernel(PrefillParams p) 
             }
             Dk::read(ch[h], m, lb, &s_scl[c & 1][0], kofs, vofs, g);
         }
-        process_chunk_d256<KV, NW, false>(st, ch, qop, cscale, 32 * c, kend, 0, min(lim, kend), g);
+        process_chunk_d256_rg<KV, RG>(st, ch, qop, cscale, 32 * c, kend, lim1, g);
         __syncthreads();                              // every wave is done with buffer c % 2
         valid_cur = valid_next;
     }
 
     // normalize and write this wave's rows: lane (i, g) holds row i's
     // d = 128h + 32g + 8r + c in acc[h][c][r]
-    float l_run = st.l;
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
-    if (live) {
-        const bool empty = !(l_run > 0.0f);
-        const float inv = empty ? 0.0f : vscale / l_run;
-        float* o = p.out + row * DW;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+    for (int j = 0; j < RG; ++j) {
+        float l_run = st[j].l;
+        l_run += shfl_xor(l_run, 16);
+        l_run += shfl_xor(l_run, 32);
+        if (live[j]) {
+            const bool empty = !(l_run > 0.0f);
+            const float inv = empty ? 0.0f : vscale / l_run;
+            float* o = p.out + row[j] * DW;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                float* dst = o + 128 * h + 32 * g + 8 * rr;
-                *reinterpret_cast<f32x4*>(dst) =
-                    f32x4{st.acc[h][0][rr], st.acc[h][1][rr], st.acc[h][2][rr], st.acc[h][3][rr]} * inv;
-                *reinterpret_cast<f32x4*>(dst + 4) =
-                    f32x4{st.acc[h][4][rr], st.acc[h][5][rr], st.acc[h][6][rr], st.acc[h][7][rr]} * inv;
-            }
-        if (g == 0) p.lse[row] = empty ? -__builtin_inff() : (st.m + __builtin_log2f(l_run)) * kLn2;
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    float* dst = o + 128 * h + 32 * g + 8 * rr;
+                    *reinterpret_cast<f32x4*>(dst) = f32x4{st[j].acc[h][0][rr], st[j].acc[h][1][rr],
+                                                           st[j].acc[h][2][rr], st[j].acc[h][3][rr]} * inv;
+                    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{st[j].acc[h][4][rr], st[j].acc[h][5][rr],
+                                                               st[j].acc[h][6][rr], st[j].acc[h][7][rr]} * inv;
+                }
+            if (g == 0) p.lse[row[j]] = empty ? -__builtin_inff() : (st[j].m + __builtin_log2f(l_run)) * kLn2;
+        }
     }
 }
 
 }  // namespace
 
 hipError_t launch_prefill256(const PrefillParams& p, hipStream_t s) {
+    constexpr int RG = 2;                               // 16-row groups per wave: 128 rows per workgroup
     const int G = p.num_q_heads / p.kv.num_kv_heads;
-    dim3 grid((unsigned)((p.max_q_len * G + 63) / 64), p.kv.num_kv_heads, p.num_seqs);
+    dim3 grid((unsigned)((p.max_q_len * G + 64 * RG - 1) / (64 * RG)), p.kv.num_kv_heads, p.num_seqs);
     switch (p.kv.dtype) {
-    case KV_FP16: hipLaunchKernelGGL(paged_prefill256_kernel<KV_FP16>, grid, dim3(256), 0, s, p); break;
-    case KV_E4M3: hipLaunchKernelGGL(paged_prefill256_kernel<KV_E4M3>, grid, dim3(256), 0, s, p); break;
-    case KV_INT8: hipLaunchKernelGGL(paged_prefill256_kernel<KV_INT8>, grid, dim3(256), 0, s, p); break;
+    case KV_FP16: hipLaunchKernelGGL((paged_prefill256_kernel<KV_FP16, RG>), grid, dim3(256), 0, s, p); break;
+    case KV_E4M3: hipLaunchKernelGGL((paged_prefill256_kernel<KV_E4M3, RG>), grid, dim3(256), 0, s, p); break;
+    case KV_INT8: hipLaunchKernelGGL((paged_prefill256_kernel<KV_INT8, RG>), grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
