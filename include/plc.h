@@ -31,13 +31,11 @@
  *    num_kv_heads with a group size G = Hq/Hkv of 1, 2, 4, 8 or 16.
  *  - head_dim 256 (1Cat-vLLM README, Layer 2 "D256 Split-D": the head is
  *    processed as two 128-wide halves; "GQA Multi-Head Packing": six query
- *    heads per KV head) is taken by plc_kv_append_quant,
- *    plc_attn_decode_partials, plc_attn_decode_paged, plc_attn_decode_append,
- *    plc_attn_verify_paged and plc_attn_window_paged, with any group size G
- *    from 1 to 16.  There the attention writes partials and merges them in a
- *    second kernel (the one of plc_lse_merge), so the workspace counters are
- *    unused.  plc_attn_prefill_paged refuses head_dim 256 with
- *    PLC_ERR_UNSUPPORTED.
+ *    heads per KV head) is taken by every entry point, with any group size G
+ *    from 1 to 16.  There the decode family (plc_attn_decode_partials,
+ *    plc_attn_decode_paged, plc_attn_decode_append, plc_attn_verify_paged,
+ *    plc_attn_window_paged) writes partials and merges them in a second
+ *    kernel (the one of plc_lse_merge), so the workspace counters are unused.
  */
 #ifndef PLC_H
 #define PLC_H
