@@ -19,8 +19,13 @@ FP16 / E4M3 / INT8, and the CPU oracle timed on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu]
 
+Further lines: verification of drafted tokens and draft-window attention at
+the decode batch's shape, and head dim 256 (groups of six query heads) decode
+in FP16 / E4M3 / INT8 and chunked prefill.
+
 Profiling aids (no bench line): --prefill-only runs and times just the chunked
 prefill; --verify-only just the verification and draft-window attention;
+--d256-only just the head dim 256 workloads;
 --copy-calibration runs a plain 256 MiB device copy five times, the
 known-size kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters.
 """
