@@ -464,9 +464,27 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(16))) f32x4 s_scl[KV == KV_INT8 ? NW : 1][2][KV == KV_INT8 ? 64 : 1];
     float* smem = reinterpret_cast<float*>(&s_dma[0][0][0]);
     __shared__ int s_last;
-    const int part = blockIdx.x, b = blockIdx.z;
-    const int kvh = MQ ? (int)blockIdx.y / p.ncg : (int)blockIdx.y;
-    const int cg = MQ ? (int)blockIdx.y - kvh * p.ncg : 0;
+    // Workgroup -> (partition, row group).  The usual grid is (partition,
+    // KV head x row group, sequence).  When the whole grid fits on the chip at
+    // once (p.xcd_local), it is one-dimensional instead and workgroup i takes
+    // group 8 (i / 8 / nparts) + i % 8 and partition (i / 8) % nparts: the
+    // hardware deals workgroups to the eight XCDs in turn (i % 8), so every
+    // partition of a group runs on one XCD, beside the group's merge.
+    int part, b, kvh, cg;
+    if (p.xcd_local) {
+        const int i8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
+        const int grp = 8 * (rest / p.nparts) + i8;
+        if (grp >= p.num_seqs * p.kv.num_kv_heads * p.ncg) return;   // padding of the last eight groups
+        part = rest % p.nparts;
+        cg = grp % p.ncg;
+        kvh = (grp / p.ncg) % p.kv.num_kv_heads;
+        b = grp / (p.ncg * p.kv.num_kv_heads);
+    } else {
+        part = blockIdx.x;
+        b = blockIdx.z;
+        kvh = MQ ? (int)blockIdx.y / p.ncg : (int)blockIdx.y;
+        cg = MQ ? (int)blockIdx.y - kvh * p.ncg : 0;
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // Chunk c of the partition goes to the wave with cw = c mod NW, cw =
@@ -1107,6 +1125,10 @@ hipError_t launch_mq(const DecodeParams& p, hipStream_t s) {
     static_assert(NW * 16384 >= 4 * NW * (32 + 16 * (D + 4)), "merge space");
     const size_t lds = 0;
     dim3 grid(p.nparts, p.kv.num_kv_heads * p.ncg, p.num_seqs);
+    if (p.xcd_local) {
+        const int64_t groups = (int64_t)p.num_seqs * p.kv.num_kv_heads * p.ncg;
+        grid = dim3((unsigned)(((groups + 7) / 8) * 8 * p.nparts), 1, 1);
+    }
     hipLaunchKernelGGL((paged_decode_kernel<KV, NW, MQ>), grid, dim3(64 * NW), lds, s, p);
     return hipGetLastError();
 }
@@ -1431,7 +1453,15 @@ hipError_t launch_prefill256(const PrefillParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s) {
+hipError_t launch_decode_partials(const DecodeParams& p0, hipStream_t s) {
+    // The XCD-local placement only when every workgroup is resident at once
+    // (one 128 KiB-LDS workgroup per CU, 256 CUs): then the dispatch order
+    // cannot delay any partition, and a group's partials stay on one XCD.
+    // Larger grids keep the sequence-major order, which starts a long
+    // sequence's partitions together.
+    DecodeParams p = p0;
+    const int64_t groups = (int64_t)p.num_seqs * p.kv.num_kv_heads * p.ncg;
+    p.xcd_local = p.kv.head_dim == 128 && ((groups + 7) / 8) * 8 * p.nparts <= 256;
     if (p.kv.head_dim == 256) {
         switch (p.kv.dtype) {
         case KV_FP16: return launch_d256<KV_FP16>(p, s);

@@ -58,6 +58,9 @@ struct DecodeParams {
     // query tokens in the call (rows = total_q_tokens * num_q_heads): num_seqs
     // for a one-token decode, cu_q_lens[num_seqs] with cu_q_lens
     int32_t total_q_tokens;
+    // set by the launcher: one-dimensional grid that keeps each group's
+    // partitions on one XCD (used when the whole grid is resident at once)
+    int32_t xcd_local;
 };
 
 hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s);
