@@ -466,19 +466,23 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     __shared__ int s_last;
     // Workgroup -> (partition, row group).  The usual grid is (partition,
     // KV head x row group, sequence).  When the whole grid fits on the chip at
-    // once (p.xcd_local), it is one-dimensional instead and workgroup i takes
-    // group 8 (i / 8 / nparts) + i % 8 and partition (i / 8) % nparts: the
-    // hardware deals workgroups to the eight XCDs in turn (i % 8), so every
-    // partition of a group runs on one XCD, beside the group's merge.
+    // once (p.xcd_local), it is one-dimensional instead: the hardware deals
+    // workgroups to the eight XCDs in turn (i % 8), and workgroup i takes the
+    // (sequence, KV head) unit 8 (i / 8 / (ncg nparts)) + i % 8, so every
+    // partition and row group of a unit runs on one XCD, beside the unit's
+    // merges; within the unit the row groups of one partition are neighbours,
+    // so the second group's page reads hit that XCD's L2.
     int part, b, kvh, cg;
     if (p.xcd_local) {
         const int i8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
-        const int grp = 8 * (rest / p.nparts) + i8;
-        if (grp >= p.num_seqs * p.kv.num_kv_heads * p.ncg) return;   // padding of the last eight groups
-        part = rest % p.nparts;
-        cg = grp % p.ncg;
-        kvh = (grp / p.ncg) % p.kv.num_kv_heads;
-        b = grp / (p.ncg * p.kv.num_kv_heads);
+        const int per_unit = p.ncg * p.nparts;
+        const int unit = 8 * (rest / per_unit) + i8;
+        if (unit >= p.num_seqs * p.kv.num_kv_heads) return;       // padding of the last eight units
+        const int within = rest % per_unit;
+        part = within / p.ncg;
+        cg = within % p.ncg;
+        kvh = unit % p.kv.num_kv_heads;
+        b = unit / p.kv.num_kv_heads;
     } else {
         part = blockIdx.x;
         b = blockIdx.z;
@@ -1126,8 +1130,8 @@ hipError_t launch_mq(const DecodeParams& p, hipStream_t s) {
     const size_t lds = 0;
     dim3 grid(p.nparts, p.kv.num_kv_heads * p.ncg, p.num_seqs);
     if (p.xcd_local) {
-        const int64_t groups = (int64_t)p.num_seqs * p.kv.num_kv_heads * p.ncg;
-        grid = dim3((unsigned)(((groups + 7) / 8) * 8 * p.nparts), 1, 1);
+        const int64_t units = (int64_t)p.num_seqs * p.kv.num_kv_heads;
+        grid = dim3((unsigned)(((units + 7) / 8) * 8 * p.ncg * p.nparts), 1, 1);
     }
     hipLaunchKernelGGL((paged_decode_kernel<KV, NW, MQ>), grid, dim3(64 * NW), lds, s, p);
     return hipGetLastError();
@@ -1460,8 +1464,8 @@ hipError_t launch_decode_partials(const DecodeParams& p0, hipStream_t s) {
     // Larger grids keep the sequence-major order, which starts a long
     // sequence's partitions together.
     DecodeParams p = p0;
-    const int64_t groups = (int64_t)p.num_seqs * p.kv.num_kv_heads * p.ncg;
-    p.xcd_local = p.kv.head_dim == 128 && ((groups + 7) / 8) * 8 * p.nparts <= 256;
+    const int64_t units = (int64_t)p.num_seqs * p.kv.num_kv_heads;
+    p.xcd_local = p.kv.head_dim == 128 && ((units + 7) / 8) * 8 * p.ncg * p.nparts <= 256;
     if (p.kv.head_dim == 256) {
         switch (p.kv.dtype) {
         case KV_FP16: return launch_d256<KV_FP16>(p, s);
