@@ -47,7 +47,21 @@
 extern "C" {
 #endif
 
-#define PLC_ABI_VERSION 1u
+#define PLC_ABI_VERSION 2u
+
+/*
+ * Every decode-family workspace (plc_attn_decode_paged / _append / _partials,
+ * plc_attn_verify_paged, plc_attn_window_paged) starts with a fixed region of
+ * PLC_WS_COUNTER_BYTES holding the int32 completion counters of the fused
+ * merge, one per (sequence, KV head, row group), at most
+ * PLC_WS_COUNTER_BYTES / 4 of them per call (more: PLC_ERR_UNSUPPORTED).  The
+ * region must be zero before the first call that uses the buffer (a
+ * zero-filled allocation is); every call that completes leaves it zero, so
+ * one buffer may serve calls of any shape in turn.  Partial outputs fp32
+ * [rows][nparts][head_dim] follow at offset PLC_WS_COUNTER_BYTES, then partial
+ * LSEs fp32 [rows][nparts], each region 256-byte aligned.
+ */
+#define PLC_WS_COUNTER_BYTES 65536
 
 /* KV storage types. */
 #define PLC_KV_FP16 0 /* fp16 values as is */
@@ -108,6 +122,10 @@ const char* plc_last_error(void);
  * INT8: sigma = max_d |x_d| / 127 per (token, head); code = clamp(rint(x /
  *       sigma), -127, 127) in fp32 (ties to even); sigma stored in the scale
  *       array at the token's slot; an all-zero row stores sigma 0, codes 0.
+ *       Attention folds 64 * sigma_v into the fp16 probability operand, so
+ *       every finite fp16 value row (sigma <= 65504/127) stays in fp16 range
+ *       (64 * 515.8 < 65504); a scale array written by other means must keep
+ *       sigma <= 1023 for the same reason.
  * FP16: copied.  A block id outside [0, num_blocks) skips that write.
  */
 int plc_kv_append_quant(const plc_kv_cache* kv, const void* k_new, const void* v_new,
@@ -139,11 +157,11 @@ int plc_attn_prefill_paged(const void* q, int32_t num_q_heads, const plc_kv_cach
                            void* stream);
 
 /*
- * Workspace bytes plc_attn_decode_paged / plc_attn_decode_partials need:
- * partial outputs fp32 [num_seqs * num_q_heads][nparts][head_dim], partial
- * LSEs fp32 [num_seqs * num_q_heads][nparts] (nparts =
- * ceil(max_context_len / partition)) and int32 completion counters
- * [num_seqs * num_q_heads], each region 256-byte aligned.
+ * Workspace bytes plc_attn_decode_paged / _append / _partials need: the
+ * counter region (PLC_WS_COUNTER_BYTES), partial outputs fp32
+ * [num_seqs * num_q_heads][nparts][head_dim] and partial LSEs fp32
+ * [num_seqs * num_q_heads][nparts] (nparts = ceil(max_context_len /
+ * partition)), each region 256-byte aligned.
  * partition_tokens = 0 picks the default partition for max_context_len
  * (plc_decode_partition_tokens).
  */
@@ -222,6 +240,11 @@ int plc_attn_decode_append(const void* q, const void* k_new, const void* v_new,
  * and lse -inf.  Calls that share a workspace must not overlap.
  */
 #define PLC_VERIFY_MAX_Q_LEN 16
+/* Capability query: the largest max_q_len plc_attn_verify_paged and
+ * plc_attn_window_paged take (PLC_VERIFY_MAX_Q_LEN of the built library; the
+ * pages' installation check prints the grouped-verify maximum query length,
+ * 1Cat-vLLM README, "Installation"). */
+int32_t plc_verify_max_query_tokens(void);
 size_t plc_verify_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
                                  int32_t max_context_len, int32_t partition_tokens);
@@ -258,7 +281,8 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
 /*
  * First half of plc_attn_decode_paged: per-partition normalized outputs and
  * LSEs into the workspace, laid out as plc_lse_merge reads them (o_parts at
- * offset 0, lse_parts at *lse_parts_offset bytes, nparts in *nparts).
+ * offset PLC_WS_COUNTER_BYTES, lse_parts at *lse_parts_offset bytes, nparts
+ * in *nparts).
  * Partitions past a sequence's end hold o = 0, lse = -inf.  Lets a caller
  * merge partials from several sources (e.g. key shards on other devices).
  * Does not touch the workspace's counters.

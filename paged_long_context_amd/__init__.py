@@ -24,7 +24,8 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libplc.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
+WS_COUNTER_BYTES = 65536   # PLC_WS_COUNTER_BYTES: the counter region at the workspace start
 
 KV_FP16, KV_E4M3, KV_INT8 = 0, 1, 2
 DTYPE_CODES = {"fp16": KV_FP16, "e4m3": KV_E4M3, "int8": KV_INT8}
@@ -88,6 +89,8 @@ _lib.plc_attn_window_paged.argtypes = [_P, _i32, _KV, _P, _i32, _P, _P, _i32, _i
                                        _i32, _f32, _P, _P, _P, _sz, _P]
 _lib.plc_lse_merge.restype = ctypes.c_int
 _lib.plc_lse_merge.argtypes = [_P, _P, _i32, _i32, _i32, _P, _P, _P]
+_lib.plc_verify_max_query_tokens.restype = _i32
+_lib.plc_verify_max_query_tokens.argtypes = []
 _lib.plc_debug_e4m3_to_f16.restype = ctypes.c_int
 _lib.plc_debug_e4m3_to_f16.argtypes = [_P, _P, _i32, _P]
 
@@ -323,12 +326,17 @@ def attn_decode_partials(q: torch.Tensor, cache: KVCache, block_tables: torch.Te
                                          ctypes.byref(nparts), ctypes.byref(off), _stream(stream)))
     n = nparts.value
     rows = B * Hq
-    o = workspace[: rows * n * D * 4].view(torch.float32).view(rows, n, D)
+    o = workspace[WS_COUNTER_BYTES: WS_COUNTER_BYTES + rows * n * D * 4].view(torch.float32).view(rows, n, D)
     l = workspace[off.value: off.value + rows * n * 4].view(torch.float32).view(rows, n)
     return o, l
 
 
 VERIFY_MAX_Q_LEN = 16
+
+
+def verify_max_query_tokens() -> int:
+    """The library's grouped-verify maximum query length (capability query)."""
+    return int(_lib.plc_verify_max_query_tokens())
 
 
 def verify_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim, max_q_len,

@@ -102,6 +102,31 @@ int hip_status(hipError_t e, const char* what) {
     return PLC_OK;
 }
 
+// Workspace layout of the decode family: the completion counters of the
+// fused merge in a fixed region at offset 0 (so a workspace reused for calls
+// of other shapes keeps them where every call expects them, zero), then the
+// partial outputs and the partial LSEs.
+void set_workspace(plc::DecodeParams* p, void* ws, size_t rows, int32_t nparts, int32_t head_dim) {
+    char* base = static_cast<char*>(ws);
+    const size_t o_bytes = align_up(rows * nparts * head_dim * sizeof(float));
+    p->counters = reinterpret_cast<int32_t*>(base);
+    p->o_parts = reinterpret_cast<float*>(base + PLC_WS_COUNTER_BYTES);
+    p->lse_parts = reinterpret_cast<float*>(base + PLC_WS_COUNTER_BYTES + o_bytes);
+}
+
+size_t partial_bytes(size_t rows, int64_t nparts, int32_t head_dim) {
+    return PLC_WS_COUNTER_BYTES + align_up(rows * nparts * head_dim * sizeof(float)) +
+           align_up(rows * nparts * sizeof(float));
+}
+
+int check_groups(int64_t groups) {
+    if (groups > PLC_WS_COUNTER_BYTES / 4)
+        return fail(PLC_ERR_UNSUPPORTED,
+                    "%lld (sequence, KV head, row group) merge groups: at most %d per call",
+                    (long long)groups, PLC_WS_COUNTER_BYTES / 4);
+    return PLC_OK;
+}
+
 int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                           int32_t partition_tokens, int32_t min_tokens = 512) {
     if (partition_tokens > 0) return partition_tokens;
@@ -129,6 +154,7 @@ int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
                     partition_tokens, kv->block_size);
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
         return fail(PLC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
+    if ((rc = check_groups((int64_t)num_seqs * kv->num_kv_heads))) return rc;
     const int32_t P = resolve_partition(num_seqs, kv->num_kv_heads, max_context_len, partition_tokens);
     const size_t need = plc_decode_workspace_size(num_seqs, num_q_heads, kv->head_dim,
                                                   max_context_len, P);
@@ -149,11 +175,7 @@ int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
     p.partition_tokens = P;
     p.nparts = nparts;
     p.qk_scale_log2 = sm_scale * 1.4426950408889634f;
-    const size_t o_bytes = align_up(rows * nparts * kv->head_dim * sizeof(float));
-    const size_t l_bytes = align_up(rows * nparts * sizeof(float));
-    p.o_parts = static_cast<float*>(workspace);
-    p.lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
-    p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + o_bytes + l_bytes);
+    set_workspace(&p, workspace, rows, nparts, kv->head_dim);
     p.out = nullptr;
     p.lse = nullptr;
     p.k_new = nullptr;
@@ -279,10 +301,8 @@ size_t plc_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
                           : resolve_partition(num_seqs, 1, max_context_len, 0);
     const int64_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
     const size_t rows = (size_t)num_seqs * num_q_heads;
-    // partial outputs, partial LSEs, and one completion counter per
-    // (sequence, KV head) -- sized per query head, which is never fewer
-    return align_up(rows * nparts * head_dim * sizeof(float)) + align_up(rows * nparts * sizeof(float)) +
-           align_up(rows * sizeof(int32_t));
+    // the counter region, partial outputs and partial LSEs
+    return partial_bytes(rows, nparts, head_dim);
 }
 
 int plc_attn_decode_partials(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
@@ -353,10 +373,9 @@ size_t plc_window_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32
     mq_partitions(num_seqs * ncg, num_kv_heads, max_q_len, max_context_len, window_tokens,
                   partition_tokens, &P, &nparts);
     const size_t rows = (size_t)total_q_tokens * num_q_heads;
-    // partial outputs and LSEs per query row, one completion counter per
-    // (sequence, KV head, row group)
-    return align_up(rows * nparts * head_dim * sizeof(float)) + align_up(rows * nparts * sizeof(float)) +
-           align_up((size_t)num_seqs * num_kv_heads * ncg * sizeof(int32_t));
+    // the counter region (one counter per (sequence, KV head, row group)),
+    // partial outputs and LSEs per query row
+    return partial_bytes(rows, nparts, head_dim);
 }
 
 size_t plc_verify_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
@@ -395,6 +414,7 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
         return fail(PLC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
     const int32_t ncg = verify_row_groups(num_q_heads, kv->num_kv_heads, max_q_len);
+    if ((rc = check_groups((int64_t)num_seqs * kv->num_kv_heads * ncg))) return rc;
     int32_t P = 0, nparts = 0;
     mq_partitions(num_seqs * ncg, kv->num_kv_heads, max_q_len, max_context_len, window_tokens,
                   partition_tokens, &P, &nparts);
@@ -417,11 +437,7 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     p.partition_tokens = P;
     p.nparts = nparts;
     p.qk_scale_log2 = sm_scale * 1.4426950408889634f;
-    const size_t o_bytes = align_up(rows * nparts * kv->head_dim * sizeof(float));
-    const size_t l_bytes = align_up(rows * nparts * sizeof(float));
-    p.o_parts = static_cast<float*>(workspace);
-    p.lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
-    p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + o_bytes + l_bytes);
+    set_workspace(&p, workspace, rows, nparts, kv->head_dim);
     p.out = out;
     p.lse = lse;
     p.k_new = nullptr;
@@ -459,6 +475,8 @@ int plc_lse_merge(const float* o_parts, const float* lse_parts, int32_t rows, in
                                             static_cast<hipStream_t>(stream)),
                       "lse merge launch");
 }
+
+int32_t plc_verify_max_query_tokens(void) { return PLC_VERIFY_MAX_Q_LEN; }
 
 int plc_debug_e4m3_to_f16(const uint8_t* codes, uint16_t* out, int32_t n, void* stream) {
     if (n < 0) return fail(PLC_ERR_INVALID_ARG, "n %d is negative", n);

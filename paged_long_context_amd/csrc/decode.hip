@@ -323,7 +323,7 @@ __device__ __forceinline__ void process_chunk(WaveState& st, Chunk<KV>& cur, con
     for (int e = 0; e < 8; ++e) {
         float pe = fast_exp2(x[e] - m_use);
         psum += pe;
-        if constexpr (KV == KV_INT8) pe *= cur.vs[e >> 2][e & 3] * 256.0f;
+        if constexpr (KV == KV_INT8) pe *= cur.vs[e >> 2][e & 3] * kInt8PFold;
         pop[e] = (f16)pe;
     }
     st.l = st.l * alpha + psum;
@@ -619,10 +619,10 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     float cscale = p.qk_scale_log2;
     if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
     // value scale applied once to the normalized output; INT8 carries its
-    // per-token scale (times 256, to keep P away from fp16 subnormals) in P
+    // per-token scale (times kInt8PFold: no fp16 overflow, few subnormals) in P
     float vscale = 1.0f;
     if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
-    if constexpr (KV == KV_INT8) vscale = 1.0f / 256.0f;
+    if constexpr (KV == KV_INT8) vscale = 1.0f / kInt8PFold;
 
     WaveState st;
     st.m = -__builtin_inff();
@@ -756,14 +756,15 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     if (!p.counters) return;
 
     // ---- fused merge: the group's last workgroup to finish combines the parts.
-    // Every thread's partial stores have completed before the counter moves
-    // (vmcnt drained, then the barrier); only the last workgroup invalidates
-    // its caches before reading the other workgroups' partials.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Publication follows the scoped memory model: the barrier orders every
+    // thread's partial stores before thread 0's counter increment, which is
+    // an agent-scope release (and acquire); the workgroup that sees the last
+    // count acquires at agent scope before reading the other workgroups'
+    // partials.  Only that workgroup pays for the cache invalidation.
     __syncthreads();
     if (tid == 0) {
         int* cnt = p.counters + ((int64_t)b * p.kv.num_kv_heads + kvh) * p.ncg + cg;
-        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == nparts_b - 1);
         if (s_last)                                   // leave the counter zeroed for the next call
             __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -839,7 +840,7 @@ __device__ __forceinline__ void process_chunk_d256(WaveState2& st, Chunk<KV> cur
     for (int e = 0; e < 8; ++e) {
         float pe = fast_exp2(x[e] - m_use);
         psum += pe;
-        if constexpr (KV == KV_INT8) pe *= cur[0].vs[e >> 2][e & 3] * 256.0f;
+        if constexpr (KV == KV_INT8) pe *= cur[0].vs[e >> 2][e & 3] * kInt8PFold;
         pop[e] = (f16)pe;
     }
     st.l = st.l * alpha + psum;
@@ -983,7 +984,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode256_kernel(DecodeParams p
     if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
     float vscale = 1.0f;
     if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
-    if constexpr (KV == KV_INT8) vscale = 1.0f / 256.0f;
+    if constexpr (KV == KV_INT8) vscale = 1.0f / kInt8PFold;
 
     WaveState2 st;
     st.m = -__builtin_inff();
@@ -1213,7 +1214,7 @@ __device__ __forceinline__ void process_chunk_d256_rg(WaveState2 st[RG], Chunk<K
         for (int e = 0; e < 8; ++e) {
             float pe = fast_exp2(x[j][e] - m_use);
             psum += pe;
-            if constexpr (KV == KV_INT8) pe *= cur[0].vs[e >> 2][e & 3] * 256.0f;
+            if constexpr (KV == KV_INT8) pe *= cur[0].vs[e >> 2][e & 3] * kInt8PFold;
             pop[j][e] = (f16)pe;
         }
         st[j].l = st[j].l * alpha + psum;
@@ -1338,7 +1339,7 @@ __global__ __launch_bounds__(256) void paged_prefill256_kernel(PrefillParams p) 
     if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
     float vscale = 1.0f;
     if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
-    if constexpr (KV == KV_INT8) vscale = 1.0f / 256.0f;
+    if constexpr (KV == KV_INT8) vscale = 1.0f / kInt8PFold;
 
     WaveState2 st[RG];
 #pragma unroll

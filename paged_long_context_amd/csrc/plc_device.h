@@ -23,6 +23,12 @@ enum KvType { KV_FP16 = 0, KV_E4M3 = 1, KV_INT8 = 2 };
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// INT8 attention folds each value row's scale sigma_v, times this factor,
+// into the fp16 probability operand (p <= 1), and divides the factor out of
+// the fp32 result.  The factor keeps typical products away from fp16
+// subnormals, and is small enough that no finite fp16 row overflows:
+// sigma_v <= 65504 / 127 = 515.8, and 64 * 515.8 = 33,011 < 65504.
+constexpr float kInt8PFold = 64.0f;
 
 // ------------------------------------------------------------------ codecs
 

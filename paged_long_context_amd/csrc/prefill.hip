@@ -267,7 +267,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
     float vscale = 1.0f;
     if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
-    if constexpr (KV == KV_INT8) vscale = 1.0f / 256.0f;
+    if constexpr (KV == KV_INT8) vscale = 1.0f / kInt8PFold;
 
     float m_ref = -__builtin_inff(), l_run = 0.0f;   // raw-score units
     const float grow_raw = (KV == KV_INT8) ? 0.0f : 8.0f / cscale;
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
             float pe = fast_exp2(__builtin_fmaf(sc[r], cscale, moff));
             psum += pe;
             if constexpr (KV == KV_INT8)   // P carries each key's value scale
-                pe *= s_vs[kb][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)] * 256.0f;
+                pe *= s_vs[kb][32 * ks + 16 * (r >> 3) + 8 * h32 + (r & 7)] * kInt8PFold;
             pprev[r >> 3][r & 7] = (f16)pe;
         }
         l_run += psum;

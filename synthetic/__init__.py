@@ -278,13 +278,19 @@ def c1_workload() -> Workload:
     return generate(spec)
 
 
-def subsample_rows(n_q: int, num_q_heads: int, count: int, seed: int, tile: int = 128) -> np.ndarray:
+def subsample_rows(n_q: int, num_q_heads: int, count: int, seed: int, tile: int = 128,
+                   every_edge: int = 0) -> np.ndarray:
     """Seeded subsample of query positions of a long chunk (row ids t*Hq+h).
 
-    Always keeps the first 8 and last 8 positions and positions on both sides
-    of tile edges; the rest are uniform without replacement.
+    Always keeps the first 8 and last 8 positions, both sides of 16 randomly
+    chosen edges of `tile`-position tiles, and (every_edge > 0) both sides of
+    every edge of `every_edge`-position tiles; the rest are uniform without
+    replacement, up to `count` positions.
     """
     keep = set(range(min(8, n_q))) | set(range(max(0, n_q - 8), n_q))
+    if every_edge > 0:
+        for e in range(every_edge, n_q, every_edge):
+            keep |= {e - 1, e}
     edges = []
     for e in range(tile, n_q, tile):
         edges += [e - 1, e]

@@ -70,7 +70,12 @@ def assert_close(o, lse, ro, rl, rows=None, what=""):
         o, ro, lse, rl = o[rows], ro[rows], lse[rows], rl[rows]
     assert np.all(np.isfinite(o)), "%s: non-finite output" % what
     err = float(np.abs(o - ro).max()) if o.size else 0.0
-    lerr = float((np.abs(lse - rl) / np.maximum(1.0, np.abs(rl))).max()) if lse.size else 0.0
+    # a row that sees no key has lse -inf on both sides; it must match exactly
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), empty), "%s: empty rows differ" % what
+    assert np.all(np.isfinite(lse[~empty])), "%s: non-finite lse" % what
+    lerr = float((np.abs(lse[~empty] - rl[~empty]) / np.maximum(1.0, np.abs(rl[~empty]))).max()) \
+        if np.any(~empty) else 0.0
     assert err <= O_ATOL, "%s: max |do| = %.3g" % (what, err)
     assert lerr <= LSE_RTOL, "%s: max rel dlse = %.3g" % (what, lerr)
     return err, lerr

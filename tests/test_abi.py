@@ -38,7 +38,9 @@ def test_library_exports_every_declared_symbol(plc):
 
 
 def test_abi_version(plc):
-    assert plc.lib().plc_abi_version() == plc.ABI_VERSION == 1
+    assert plc.lib().plc_abi_version() == plc.ABI_VERSION == 2
+    assert plc.WS_COUNTER_BYTES == 65536
+    assert plc.verify_max_query_tokens() == plc.VERIFY_MAX_Q_LEN == 16
 
 
 def _desc(plc, dtype=1, head_dim=128, block_size=16, num_blocks=10, hkv=1, scales=True):
@@ -105,10 +107,11 @@ def test_null_query_refused(plc):
 
 
 def test_workspace_size_formula(plc):
-    # rows * nparts * D floats + rows * nparts floats, each 256-byte aligned
+    # the fixed counter region, then rows * nparts * D floats and rows *
+    # nparts floats, each 256-byte aligned
     rows, nparts = 8 * 8, 16
     want = ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
-    want += ((rows * 4 + 255) // 256) * 256
+    want += 65536
     assert plc.decode_workspace_size(8, 8, 128, 32768, 2048) == want
 
 
@@ -160,7 +163,7 @@ def test_verify_workspace_size_formula(plc):
     # 4 x 8 = 32 rows per (sequence, KV head) = 2 groups of 16 -> 16 counters
     rows, nparts = 8 * 4 * 8, 16
     want = ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
-    want += ((8 * 1 * 2 * 4 + 255) // 256) * 256
+    want += 65536                                                    # counter region
     assert plc.verify_workspace_size(8, 32, 8, 1, 128, 4, 32768, 2048) == want
     assert plc.verify_workspace_size(8, 32, 8, 1, 128, 0, 32768, 2048) == 0
     assert plc.verify_workspace_size(8, 32, 8, 1, 128, 17, 32768, 2048) == 0
@@ -179,3 +182,12 @@ def test_head_dim_256_entry_points(plc):
                                     0.1, 0x1, 0x1, None) == -1      # validated up to the null q
     assert _verify(plc, d, hq=12, ws=None) == -3                      # validation passed up to the workspace
     assert _decode(plc, _desc(plc, head_dim=192)) == -2 and "head_dim" in _err(plc)
+
+
+def test_too_many_merge_groups_refused(plc):
+    # one completion counter per (sequence, KV head, row group) in the fixed
+    # 64 KiB region: 16,384 groups at most per call
+    d = _desc(plc, hkv=8)
+    assert plc.lib().plc_attn_decode_paged(0x3000, 64, ctypes.byref(d), 0x4000, 4, 0x5000, 2049, 64,
+                                           0, 0.088, 0x6000, 0x7000, 0x2000, 1 << 40, None) == -2
+    assert "merge groups" in _err(plc)

@@ -57,3 +57,27 @@ def test_d256_numerators():
                                              8 * 12 * 256 * 2 + 8 * 12 * 257 * 4)
     wp = synthetic.generate(SPECS["d256_prefill"])
     assert bench.prefill_flops(wp) == 4 * 256 * 12 * (8192 * 122880 + 8192 * 8193 // 2)
+
+
+def test_accuracy_summary():
+    ro = np.zeros((3, 2, 4), np.float32)
+    rl = np.array([[0.5, 100.0], [2.0, -1.0], [0.0, 0.0]], np.float32)
+    o = ro.copy()
+    o[1, 1, 3] = 1.5e-3
+    l = rl.copy()
+    l[0, 1] += 0.02                    # 2e-4 relative at |lse| = 100
+    a = bench.accuracy(o, l, ro, rl)
+    assert a["rows_checked"] == 6 and abs(a["max_abs_do"] - 1.5e-3) < 1e-9
+    assert abs(a["max_rel_dlse"] - 2e-4) < 1e-6 and not a["within_tolerance"]
+    a = bench.accuracy(o, l, ro, rl, rows=np.array([2, 3, 4]))
+    assert a["rows_checked"] == 3 and a["max_abs_do"] == np.float32(1.5e-3) and a["within_tolerance"]
+
+
+def test_smi_flattening_keeps_clocks_and_power():
+    sample = [{"gpu": 0, "power": {"socket_power": {"value": 612, "unit": "W"}, "gfx_voltage": "N/A"},
+               "clock": {"gfx_0": {"clk": {"value": 2100, "unit": "MHz"}},
+                         "mem_0": {"clk": {"value": 1900, "unit": "MHz"}}}}]
+    f = bench.smi_filter(sample)
+    assert f["0.power.socket_power"] == 612
+    assert f["0.clock.gfx_0.clk"] == 2100 and f["0.clock.mem_0.clk"] == 1900
+    assert "0.power.gfx_voltage" not in f

@@ -6,6 +6,7 @@ positions that always includes the first and last positions and positions on
 both sides of tile edges.  The launch configurations are the ones bench.py
 times.
 """
+import functools
 import time
 
 import numpy as np
@@ -32,9 +33,16 @@ def log(msg):
     print(msg, flush=True)
 
 
+@functools.lru_cache(maxsize=None)
+def workload(name):
+    """Each full-size workload is drawn once per test session (the draws are
+    seeded, so every test sees the same inputs)."""
+    return synthetic.generate(SPECS[name])
+
+
 def decode_config(plc, name, dtype, partition):
     t0 = time.time()
-    w = synthetic.generate(SPECS[name])
+    w = workload(name)
     cache, bt = device_cache(plc, w, dtype, upto="prefix")
     append_new(plc, cache, w, bt)              # the step's own token
     o, l = plc.attn_decode_paged(dev(w.q), cache, bt, dev(w.context_lens),
@@ -93,8 +101,52 @@ def test_c3_chunked_prefill_subsample(plc):
     torch.cuda.synchronize()
     o, l = host(o), host(l)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
-    rows = synthetic.subsample_rows(8192, 8, 256, seed=0xC3, tile=32)
+    # 512 positions x 8 heads: the first and last 8, both sides of every
+    # 128-position tile edge, 16 edge pairs of the kernel's 32-position
+    # workgroups, the rest uniform
+    rows = synthetic.subsample_rows(8192, 8, 512, seed=0xC3, tile=32, every_edge=128)
+    assert len(rows) == 4096
     ref = cases.oracle_cache(w, "e4m3")
     ro, rl = cases.oracle_attention(w, ref, sm_scale(), rows=rows)
     err = assert_close(o, l, ro, rl, rows=rows, what="c3")
     log("c3: %d rows, max|do| %.2e  rel dlse %.2e  (%.1fs)" % (len(rows), err[0], err[1], time.time() - t0))
+
+
+# The call bench.py times for a decode step: plc_attn_decode_append (the
+# step's token appended inside the decode launch, fused merge) at full size
+# in the partition bench.py resolves (2,048 for the 8 x 32K batch, automatic
+# otherwise), for every KV dtype.
+STEP_CASES = [("c2", 2048, dt) for dt in ("fp16", "e4m3", "int8")] + \
+             [("c4", 0, dt) for dt in ("fp16", "e4m3", "int8")] + \
+             [("c5", 0, dt) for dt in ("fp16", "e4m3", "int8")]
+
+
+@pytest.mark.parametrize("name,partition,dtype", STEP_CASES)
+def test_decode_step_in_one_launch_full_size(plc, name, partition, dtype):
+    t0 = time.time()
+    w = workload(name)
+    s = w.spec
+    maxc = int(w.context_lens.max())
+    P = plc.decode_partition_tokens(s.num_seqs, s.num_kv_heads, maxc, partition)
+    cache, bt = device_cache(plc, w, dtype, upto="prefix")
+    kn, vn = w.new_kv()
+    q, ctx = dev(w.q), dev(w.context_lens)
+    o, l = plc.attn_decode_append(q.view(s.num_seqs, s.num_q_heads, s.head_dim), dev(kn), dev(vn), cache, bt,
+                                  ctx, maxc, P, sm_scale())
+    # the same cache decoded again by the two-launch form's decode call
+    o2, l2 = plc.attn_decode_paged(q.view(s.num_seqs, s.num_q_heads, s.head_dim), cache, bt, ctx, maxc, P,
+                                   sm_scale())
+    torch.cuda.synchronize()
+    o, l, o2, l2 = host(o), host(l), host(o2), host(l2)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2), "fused step != decode of the appended cache"
+    ref = cases.oracle_cache(w, dtype)
+    # every slot of the cache, the appended tokens and the untouched poison included
+    assert np.array_equal(host(cache.k).view(np.uint8), ref.k.view(np.uint8)), "%s %s K" % (name, dtype)
+    assert np.array_equal(host(cache.v).view(np.uint8), ref.v.view(np.uint8)), "%s %s V" % (name, dtype)
+    if dtype == "int8":
+        for a, b in ((cache.k_scale, ref.k_tok_scale), (cache.v_scale, ref.v_tok_scale)):
+            assert np.array_equal(host(a).view(np.uint32), b.view(np.uint32)), "%s int8 scales" % name
+    ro, rl = cases.oracle_attention(w, ref, sm_scale())
+    err = assert_close(o, l, ro, rl, what="%s %s step" % (name, dtype))
+    log("%s %s step (P=%d): max|do| %.2e  rel dlse %.2e  (%.1fs)" % (name, dtype, P, err[0], err[1],
+                                                                    time.time() - t0))

@@ -312,3 +312,25 @@ def test_window_equals_key_range_per_row():
     o1, l1 = cases.oracle_attention(w, c, 0.088, window=64)
     o2, l2 = cases.oracle_attention(w, c, 0.088, key_begin=500 - 64)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_row_subset_equals_full_evaluation(dtype):
+    """The rows= path (used by the long-chunk parity tests) writes, at every
+    listed row, exactly what a full evaluation writes there, and leaves every
+    other row untouched (NaN).  The subset is unsorted, skips rows, crosses
+    sequences and heads, and includes the first and last rows, so a mix-up
+    of the listed row id with its list index fails."""
+    w = synthetic.generate(cases.spec([37, 64, 17], [37, 3, 5], hq=4, hkv=2, d=16, seed=23))
+    c = cases.oracle_cache(w, dtype)
+    full_o, full_l = cases.oracle_attention(w, c)
+    n = w.total_q * 4
+    rows = np.array([n - 1, 0, 7, 150, 3, 101, 41, 42, 168, n - 2], np.int64)
+    assert len(set(rows.tolist())) == len(rows) and rows.max() < n
+    for nthreads in (1, 3):
+        o, l = cases.oracle_attention(w, c, rows=rows, nthreads=nthreads)
+        fo, fl = o.reshape(n, -1), l.reshape(n)
+        assert np.array_equal(fo[rows], full_o.reshape(n, -1)[rows])
+        assert np.array_equal(fl[rows], full_l.reshape(n)[rows])
+        others = np.setdiff1d(np.arange(n), rows)
+        assert np.all(np.isnan(fo[others])) and np.all(np.isnan(fl[others]))
