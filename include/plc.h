@@ -216,6 +216,29 @@ int plc_attn_decode_append(const void* q, const void* k_new, const void* v_new,
                            void* stream);
 
 /*
+ * plc_attn_decode_append for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results without a workspace.  The
+ * library's own device scratch of PLC_NOALLOC_SCRATCH_BYTES stands in for it
+ * (held by every device the library runs on until the process ends); its
+ * address is looked up, and its counter region cleared by a kernel on
+ * `stream`, on the first call on each device.  The call allocates nothing.
+ *  A call that needs more than PLC_NOALLOC_SCRATCH_BYTES
+ *      (plc_decode_workspace_size > it) returns PLC_ERR_WORKSPACE.
+ *  Every call on one device shares that device's scratch: calls that overlap
+ *      in time on one device (other streams, other threads) race and give
+ *      wrong results; serialize them.  Each completed call leaves the counter
+ *      region zero for the next.
+ */
+#define PLC_NOALLOC_SCRATCH_BYTES (16 << 20)
+int plc_attn_decode_append_noalloc(const void* q, const void* k_new, const void* v_new,
+                                   int32_t num_q_heads, const plc_kv_cache* kv,
+                                   const int32_t* block_tables, int32_t max_blocks,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t max_context_len, int32_t partition_tokens, float sm_scale,
+                                   float* out, float* lse, void* stream);
+
+/*
  * Verification decode (speculative decoding: the target model scores several
  * drafted tokens per sequence in one step; ReVolta 0.1.2 release notes, the
  * DFlash2 settings that verify 3, 4 or 7 drafts per request; 1Cat-vLLM README,

@@ -74,6 +74,9 @@ _lib.plc_attn_decode_paged.argtypes = [_P, _i32, _KV, _P, _i32, _P, _i32, _i32, 
 _lib.plc_attn_decode_append.restype = ctypes.c_int
 _lib.plc_attn_decode_append.argtypes = [_P, _P, _P, _i32, _KV, _P, _i32, _P, _i32, _i32, _i32, _f32,
                                         _P, _P, _P, _sz, _P]
+_lib.plc_attn_decode_append_noalloc.restype = ctypes.c_int
+_lib.plc_attn_decode_append_noalloc.argtypes = [_P, _P, _P, _i32, _KV, _P, _i32, _P, _i32, _i32, _i32,
+                                                _f32, _P, _P, _P]
 _lib.plc_attn_decode_partials.restype = ctypes.c_int
 _lib.plc_attn_decode_partials.argtypes = [_P, _i32, _KV, _P, _i32, _P, _i32, _i32, _i32, _f32, _P,
                                           _sz, ctypes.POINTER(_i32), ctypes.POINTER(_sz), _P]
@@ -303,6 +306,39 @@ def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor
                                        B, int(max_context_len), int(partition_tokens),
                                        float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                        workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # PLC_NOALLOC_SCRATCH_BYTES
+
+
+def attn_decode_append_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                               cache: KVCache, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                               max_context_len: int, partition_tokens: int = 0,
+                               sm_scale: Optional[float] = None, out=None, lse=None, stream=None):
+    """attn_decode_append without a workspace: the library's per-device scratch
+    stands in (calls on one device must not overlap in time)."""
+    B, Hq, D = q.shape
+    _need(q, "q", torch.float16)
+    _need(k_new, "k_new", torch.float16, (B, cache.num_kv_heads, D))
+    _need(v_new, "v_new", torch.float16, (B, cache.num_kv_heads, D))
+    _need(block_tables, "block_tables", torch.int32)
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    if block_tables.shape[0] != B:
+        raise ValueError("block_tables rows %d != num_seqs %d" % (block_tables.shape[0], B))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Hq, D))
+    _need(lse, "lse", torch.float32, (B, Hq))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    _check(_lib.plc_attn_decode_append_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), Hq, cache.desc(),
+                                               _ptr(block_tables), block_tables.shape[1],
+                                               _ptr(context_lens), B, int(max_context_len),
+                                               int(partition_tokens), float(sm_scale), _ptr(out),
+                                               _ptr(lse), _stream(stream)))
     return out, lse
 
 

@@ -10,9 +10,17 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/plc.h"
 #include "plc_internal.h"
+
+// Device scratch of plc_attn_decode_append_noalloc: the decode workspace
+// (counter region, partial outputs, partial LSEs) for callers that cannot
+// allocate one.  Every device the library runs on holds its own copy until
+// the process ends.  In host code this name is only a handle for
+// hipGetSymbolAddress; kernels get the device address it returns.
+static __device__ __align__(256) unsigned char scratch[PLC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -209,6 +217,34 @@ void mq_partitions(int32_t groups, int32_t num_kv_heads, int32_t max_q_len, int3
     if (*nparts < 1) *nparts = 1;
 }
 
+// Per-device address of `scratch`, looked up (and its counter region
+// cleared by a kernel on the caller's stream) on the first call on each
+// device, with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(hipStream_t s, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PLC_ERR_UNSUPPORTED, "device %d: the no-allocation scratch serves devices 0..%d", dev,
+                    kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                       "hipGetSymbolAddress(scratch)");
+        e = plc::launch_fill_zero(ptr, PLC_WS_COUNTER_BYTES, s);
+        if (e != hipSuccess) return hip_status(e, "clearing the scratch counters");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return PLC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -357,6 +393,30 @@ int plc_attn_decode_append(const void* q, const void* k_new, const void* v_new,
     p.v_new = v_new;
     return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)),
                       "decode-append launch");
+}
+
+int plc_attn_decode_append_noalloc(const void* q, const void* k_new, const void* v_new,
+                                   int32_t num_q_heads, const plc_kv_cache* kv,
+                                   const int32_t* block_tables, int32_t max_blocks,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t max_context_len, int32_t partition_tokens, float sm_scale,
+                                   float* out, float* lse, void* stream) {
+    if (!kv) return fail(PLC_ERR_INVALID_ARG, "kv cache descriptor is NULL");
+    const size_t need = plc_decode_workspace_size(num_seqs, num_q_heads, kv->head_dim, max_context_len,
+                                                  partition_tokens);
+    if (need == 0) return fail(PLC_ERR_INVALID_ARG, "num_seqs %d / num_q_heads %d / max_context_len %d",
+                               num_seqs, num_q_heads, max_context_len);
+    if (need > (size_t)PLC_NOALLOC_SCRATCH_BYTES)
+        return fail(PLC_ERR_WORKSPACE,
+                    "this decode needs %zu bytes of scratch; the no-allocation entry point has %d "
+                    "(use plc_attn_decode_append with a workspace)",
+                    need, PLC_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const int rc = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws);
+    if (rc) return rc;
+    return plc_attn_decode_append(q, k_new, v_new, num_q_heads, kv, block_tables, max_blocks, context_lens,
+                                  num_seqs, max_context_len, partition_tokens, sm_scale, out, lse, ws,
+                                  PLC_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t plc_window_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,

@@ -102,6 +102,9 @@ struct PrefillParams {
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill256(const PrefillParams& p, hipStream_t s);   // head dim 256
 
+// zero `bytes` (a multiple of 16, 16-byte aligned) with a kernel
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
 hipError_t launch_debug_e4m3(const uint8_t* codes, uint16_t* out, int32_t n, hipStream_t s);
 
 }  // namespace plc

@@ -191,3 +191,15 @@ def test_too_many_merge_groups_refused(plc):
     assert plc.lib().plc_attn_decode_paged(0x3000, 64, ctypes.byref(d), 0x4000, 4, 0x5000, 2049, 64,
                                            0, 0.088, 0x6000, 0x7000, 0x2000, 1 << 40, None) == -2
     assert "merge groups" in _err(plc)
+
+
+def test_no_alloc_refuses_more_than_its_scratch(plc):
+    # 1024 sequences x 32 heads x 16 partitions of partials need ~270 MB,
+    # beyond the 16 MiB scratch: refused on the host before any launch
+    d = _desc(plc, hkv=4)
+    L = plc.lib()
+    assert L.plc_attn_decode_append_noalloc(0x3000, 0x3100, 0x3200, 32, ctypes.byref(d), 0x4000, 8192,
+                                            0x5000, 1024, 131072, 8192, 0.088, 0x6000, 0x7000,
+                                            None) == -3
+    assert "scratch" in _err(plc) and str(16 << 20) in _err(plc)
+    assert plc.NOALLOC_SCRATCH_BYTES == 16 << 20
