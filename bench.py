@@ -227,27 +227,59 @@ SMI_KEYS = ("clk", "clock", "freq", "power", "cap", "limit")
 
 
 def smi_filter(data):
+    """Current clocks and power of an `amd-smi metric --clock --power` reading
+    (min/max clock bounds and non-numeric fields dropped)."""
     flat = _flatten(data)
-    keep = {k: v for k, v in flat.items()
-            if any(t in k.lower() for t in SMI_KEYS) and not isinstance(v, str) or
-            ("throttle" in k.lower())}
-    return dict(list(keep.items())[:80])
+    keep = {}
+    for k, v in flat.items():
+        kl = k.lower()
+        if isinstance(v, str) or kl.endswith(("min_clk", "max_clk")):
+            continue
+        if any(t in kl for t in SMI_KEYS):
+            keep[k.replace("gpu_data.0.", "")] = v
+    return dict(list(keep.items())[:60])
 
 
 def smi_static():
-    d, err = _smi(["static", "-g", "0", "--limit"])
-    return smi_filter(d) if d is not None else {"error": err}
+    """Board identity and clock levels (amd-smi static) and the power cap (rocm-smi)."""
+    out = {}
+    d, err = _smi(["static", "-g", "0"])
+    if d is None:
+        out["amd_smi_static_error"] = err
+    else:
+        flat = _flatten(d)
+        for k, v in flat.items():
+            kl = k.lower()
+            if kl.endswith(("market_name", "product_name")) or ".ifwi.name" in kl or \
+                    (".clock." in kl and ("frequency_levels" in kl) and (".sys." in kl or ".mem." in kl)):
+                out[k] = v
+    try:
+        r = subprocess.run(["rocm-smi", "--showmaxpower", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        j = json.loads(r.stdout)
+        out.update({"rocm_smi." + k: v for k, v in _flatten(j).items() if "power" in k.lower()})
+    except Exception as e:
+        out["rocm_smi_error"] = "%s: %s" % (type(e).__name__, str(e)[:200])
+    return out
 
 
-def smi_under_load(replay, max_s=8.0):
-    """GPU clocks and power read by amd-smi while `replay` keeps the GPU busy."""
+def smi_under_load(replay, max_s=8.0, warm_s=0.3):
+    """GPU clocks and power read by amd-smi while `replay` keeps the GPU busy
+    (busy for warm_s before the reading starts, so the clocks have ramped)."""
+    n = 0
+    t_warm = time.time() + warm_s
+    while time.time() < t_warm:
+        replay()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
     try:
         p = subprocess.Popen(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"],
                              stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
     except Exception as e:
+        torch.cuda.synchronize()
         return {"error": "%s: %s" % (type(e).__name__, e)}
     t_end = time.time() + max_s
-    n = 0
     while p.poll() is None and time.time() < t_end:
         replay()
         n += 1

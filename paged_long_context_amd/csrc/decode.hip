@@ -757,17 +757,20 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
 
     // ---- fused merge: the group's last workgroup to finish combines the parts.
     // Publication follows the scoped memory model: the barrier orders every
-    // thread's partial stores before thread 0's counter increment, which is
-    // an agent-scope release (and acquire); the workgroup that sees the last
-    // count acquires at agent scope before reading the other workgroups'
-    // partials.  Only that workgroup pays for the cache invalidation.
+    // thread's partial stores before thread 0's counter increment, an
+    // agent-scope release; the thread that sees the last count issues an
+    // agent-scope acquire before the barrier that lets its workgroup read
+    // the other workgroups' partials.  Only that workgroup pays for the
+    // cache invalidation.
     __syncthreads();
     if (tid == 0) {
         int* cnt = p.counters + ((int64_t)b * p.kv.num_kv_heads + kvh) * p.ncg + cg;
-        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == nparts_b - 1);
-        if (s_last)                                   // leave the counter zeroed for the next call
+        if (s_last) {                                 // leave the counter zeroed for the next call
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __syncthreads();
     if (!s_last) return;
@@ -1133,6 +1136,20 @@ hipError_t launch_mq(const DecodeParams& p, hipStream_t s) {
     if (p.xcd_local) {
         const int64_t units = (int64_t)p.num_seqs * p.kv.num_kv_heads;
         grid = dim3((unsigned)(((units + 7) / 8) * 8 * p.ncg * p.nparts), 1, 1);
+    }
+    if (p.counters && !p.xcd_local) {
+        // A grid larger than the chip holds at once: the partitions, then
+        // the merge kernel.  Fused, every workgroup's agent-scope release
+        // (an L2 write-back) would be paid thousands of times per step
+        // (measured +25 us on the ragged 32-sequence step); the kernel
+        // boundary orders the partials for free.
+        DecodeParams q = p;
+        q.counters = nullptr;
+        hipLaunchKernelGGL((paged_decode_kernel<KV, NW, MQ>), grid, dim3(64 * NW), lds, s, q);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_lse_merge(p.o_parts, p.lse_parts, p.total_q_tokens * p.num_q_heads, p.nparts, D, p.out,
+                                p.lse, s);
     }
     hipLaunchKernelGGL((paged_decode_kernel<KV, NW, MQ>), grid, dim3(64 * NW), lds, s, p);
     return hipGetLastError();

@@ -78,6 +78,6 @@ def test_smi_flattening_keeps_clocks_and_power():
                "clock": {"gfx_0": {"clk": {"value": 2100, "unit": "MHz"}},
                          "mem_0": {"clk": {"value": 1900, "unit": "MHz"}}}}]
     f = bench.smi_filter(sample)
-    assert f["0.power.socket_power"] == 612
+    assert f["0.power.socket_power"] == 612 and "0.clock.gfx_0.max_clk" not in f
     assert f["0.clock.gfx_0.clk"] == 2100 and f["0.clock.mem_0.clk"] == 1900
     assert "0.power.gfx_voltage" not in f
