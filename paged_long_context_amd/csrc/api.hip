@@ -127,6 +127,23 @@ size_t partial_bytes(size_t rows, int64_t nparts, int32_t head_dim) {
            align_up(rows * nparts * sizeof(float));
 }
 
+// A fused-merge launch of at most this many workgroup slots (rounded units of
+// eight (sequence, KV head) groups x row groups x partitions) leaves compute
+// units idle on the 256-CU chip; the launcher then streams each partition
+// with two workgroups, and the workspace holds partials for 2 nparts.
+bool may_split_partitions(int64_t units, int32_t ncg, int64_t nparts, int32_t partition_tokens) {
+    return ((units + 7) / 8) * 8 * ncg * nparts * 2 <= 256 && partition_tokens % 64 == 0 &&
+           partition_tokens >= 512;
+}
+
+// Partial bytes of a decode-family call: doubled partitions when the launch
+// may split them.
+size_t decode_partial_bytes(size_t rows, int64_t units, int32_t ncg, int64_t nparts, int32_t partition_tokens,
+                            int32_t head_dim) {
+    const bool split = may_split_partitions(units, ncg, nparts, partition_tokens);
+    return partial_bytes(rows, split ? 2 * nparts : nparts, head_dim);
+}
+
 int check_groups(int64_t groups) {
     if (groups > PLC_WS_COUNTER_BYTES / 4)
         return fail(PLC_ERR_UNSUPPORTED,
@@ -184,6 +201,8 @@ int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
     p.nparts = nparts;
     p.qk_scale_log2 = sm_scale * 1.4426950408889634f;
     set_workspace(&p, workspace, rows, nparts, kv->head_dim);
+    p.may_split = workspace_bytes >= partial_bytes(rows, 2 * (int64_t)nparts, kv->head_dim) ? 1 : 0;
+    if (p.may_split) set_workspace(&p, workspace, rows, 2 * nparts, kv->head_dim);
     p.out = nullptr;
     p.lse = nullptr;
     p.k_new = nullptr;
@@ -337,8 +356,9 @@ size_t plc_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
                           : resolve_partition(num_seqs, 1, max_context_len, 0);
     const int64_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
     const size_t rows = (size_t)num_seqs * num_q_heads;
-    // the counter region, partial outputs and partial LSEs
-    return partial_bytes(rows, nparts, head_dim);
+    // the counter region, partial outputs and partial LSEs; sized for one KV
+    // head (the fewest units, so the split partitions whenever they may occur)
+    return decode_partial_bytes(rows, num_seqs, 1, nparts, P, head_dim);
 }
 
 int plc_attn_decode_partials(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
@@ -435,7 +455,7 @@ size_t plc_window_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32
     const size_t rows = (size_t)total_q_tokens * num_q_heads;
     // the counter region (one counter per (sequence, KV head, row group)),
     // partial outputs and LSEs per query row
-    return partial_bytes(rows, nparts, head_dim);
+    return decode_partial_bytes(rows, (int64_t)num_seqs * num_kv_heads, ncg, nparts, P, head_dim);
 }
 
 size_t plc_verify_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
@@ -498,6 +518,8 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     p.nparts = nparts;
     p.qk_scale_log2 = sm_scale * 1.4426950408889634f;
     set_workspace(&p, workspace, rows, nparts, kv->head_dim);
+    p.may_split = workspace_bytes >= partial_bytes(rows, 2 * (int64_t)nparts, kv->head_dim) ? 1 : 0;
+    if (p.may_split) set_workspace(&p, workspace, rows, 2 * nparts, kv->head_dim);
     p.out = out;
     p.lse = lse;
     p.k_new = nullptr;

@@ -562,42 +562,57 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     const int nblk = (tok1 - tok0 + BS - 1) / BS;
     const int nchunks = (nblk + 1) / 2;
 
+    // Fused append: the partition that holds the step's own token (position
+    // L - 1) writes it to its page, quantized exactly as plc_kv_append_quant
+    // does, by the wave that owns the token's chunk (lanes 0-15: K, 16-31: V,
+    // eight values each).  That wave does not wait for the stores: it keeps
+    // the codes (and INT8 scales) in registers and writes them over the
+    // token's row in its LDS copy of the chunk once the chunk's pages have
+    // landed, so whatever the page loads saw of the row does not matter.  No
+    // other wave reads that page.
     const bool appends = p.k_new != nullptr && part == (L - 1) / P;     // uniform in the workgroup
-    if (appends && cw == ((L - 1 - tok0) / 32) % NW) {
-        // Fused append: this partition holds the step's own token (position
-        // L - 1) and this wave owns its chunk, the only one that reads that
-        // page.  Quantize the token's K and V exactly as plc_kv_append_quant
-        // does, write them to their page, and let the stores complete before
-        // this wave loads anything.  The codes of one page share no cache line
-        // with another page's, so the other waves need not wait; INT8 scale
-        // rows of neighbouring pages do share lines, so for INT8 the whole
-        // workgroup waits (below) before anyone loads.
-        if (lane < 32) {
-            const int which = lane >> 4, sl = lane & 15;
-            const int pos = L - 1;
-            const int pg = bt[pos / BS];
-            const f16x8 x = *reinterpret_cast<const f16x8*>(
-                static_cast<const f16*>(which ? p.v_new : p.k_new) + ((int64_t)b * p.kv.num_kv_heads + kvh) * D +
-                8 * sl);
-            if (pg >= 0 && pg < p.kv.num_blocks) {
-                const int64_t crow = ((int64_t)pg * p.kv.num_kv_heads + kvh) * BS + (pos % BS);
-                void* cache = const_cast<void*>(which ? p.kv.v : p.kv.k);
-                if constexpr (KV == KV_FP16) {
-                    *reinterpret_cast<f16x8*>(static_cast<f16*>(cache) + crow * D + 8 * sl) = x;
-                } else {
-                    float s = 1.0f, sigma = 0.0f;
-                    if constexpr (KV == KV_E4M3) s = (which ? p.kv.v_scale : p.kv.k_scale)[kvh];
-                    const u32x2 w = quantize_slice<KV>(x, s, sigma);
-                    *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(cache) + crow * D + 8 * sl) = w;
-                    if constexpr (KV == KV_INT8)
-                        if (sl == 0) const_cast<float*>(which ? p.kv.v_scale : p.kv.k_scale)[crow] = sigma;
-                }
+    const int tok_chunk = appends ? (L - 1 - tok0) / 32 : -1;           // chunk index in the partition
+    const bool app_wave = appends && cw == tok_chunk % NW;
+    u32x2 app_codes = u32x2{0, 0};                                      // 8-bit codes of the lane's slice
+    f16x8 app_x = f16x8{0, 0, 0, 0, 0, 0, 0, 0};                         // FP16 values of the lane's slice
+    float app_sigma = 0.0f;                                             // INT8 scale (lanes 0 and 16)
+    if (app_wave && lane < 32) {
+        const int which = lane >> 4, sl = lane & 15;
+        const int pos = L - 1;
+        const int pg = bt[pos / BS];
+        app_x = *reinterpret_cast<const f16x8*>(
+            static_cast<const f16*>(which ? p.v_new : p.k_new) + ((int64_t)b * p.kv.num_kv_heads + kvh) * D + 8 * sl);
+        if constexpr (KV != KV_FP16) {
+            float sc = 1.0f;
+            if constexpr (KV == KV_E4M3) sc = (which ? p.kv.v_scale : p.kv.k_scale)[kvh];
+            app_codes = quantize_slice<KV>(app_x, sc, app_sigma);
+        }
+        if (pg >= 0 && pg < p.kv.num_blocks) {
+            const int64_t crow = ((int64_t)pg * p.kv.num_kv_heads + kvh) * BS + (pos % BS);
+            void* cache = const_cast<void*>(which ? p.kv.v : p.kv.k);
+            if constexpr (KV == KV_FP16) {
+                *reinterpret_cast<f16x8*>(static_cast<f16*>(cache) + crow * D + 8 * sl) = app_x;
+            } else {
+                *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(cache) + crow * D + 8 * sl) = app_codes;
+                if constexpr (KV == KV_INT8)
+                    if (sl == 0) const_cast<float*>(which ? p.kv.v_scale : p.kv.k_scale)[crow] = app_sigma;
             }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    if constexpr (KV == KV_INT8)
-        if (appends) __syncthreads();
+    // the token's row inside its chunk: page tpg, row tr
+    const int t_in = appends ? (L - 1) - (tok0 + 32 * tok_chunk) : 0;
+    const int tpg = t_in >> 4, tr = t_in & 15;
+    // FP16 V reaches registers, not LDS: every lane (i, g) takes the V slice
+    // d = 8i.. from lane 16 + i, for when g holds the token's row (token 4g +
+    // e%4 of page e/4 in register e)
+    u32x4 app_v = u32x4{0, 0, 0, 0};
+    if constexpr (KV == KV_FP16)
+        if (app_wave) {
+            const u32x4 xs = __builtin_bit_cast(u32x4, app_x);
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                app_v[w] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 + i) << 2, (int)xs[w]);
+        }
 
     // Q^T operand: lane (i, g) holds row (column) i, d = 64*(kc/2) + 16g +
     // 8*(kc%2) + [0, 8); its causal limit: position L - n + j sees keys below
@@ -674,8 +689,41 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
             Dk::issue(m, &s_dma[wave][b][0], &s_scl[KV == KV_INT8 ? wave : 0][b][0], p, kvh, __builtin_amdgcn_readlane(tbl, 2 * k),
                       __builtin_amdgcn_readlane(tbl, 2 * k + 1), 2 * ch + 1 < nblk, lane, dsrc);
         };
-        typename Dk::Meta ma, mb;
+        // consume chunk k of the segment from buffer bf: the appending wave
+        // first writes the step's token over its row (after the pages landed)
         Chunk<KV> c;
+        auto consume = [&](typename Dk::Meta& m, int bf, int k) __attribute__((always_inline)) {
+            const int ch = cw + (seg + k) * NW;
+            uint8_t* lb = &s_dma[wave][bf][0];
+            f32x4* sb = &s_scl[KV == KV_INT8 ? wave : 0][bf][0];
+            const bool patch = app_wave && ch == tok_chunk;                 // uniform
+            if (patch) {
+                if constexpr (KV == KV_FP16) {
+                    if (lane < 16)                      // K row tr: chunk sl at slot sl ^ tr
+                        *reinterpret_cast<f16x8*>(lb + 4096 * tpg + 256 * tr + 16 * (lane ^ tr)) = app_x;
+                } else {
+                    const int srow = Dk::swap02(tr);
+                    if (lane < 32) {
+                        const int which = lane >> 4, sl = lane & 15;
+                        *reinterpret_cast<u32x2*>(lb + 4096 * which + 2048 * tpg + 128 * srow +
+                                                  16 * ((sl >> 1) ^ Dk::kap(srow)) + 8 * (sl & 1)) = app_codes;
+                    }
+                    if constexpr (KV == KV_INT8)
+                        if (lane == 0 || lane == 16)    // [K | V][page][4 tokens] slots of f32x4
+                            reinterpret_cast<float*>(sb)[4 * (((lane >> 4) << 3) | (tpg << 2) | (tr >> 2)) + (tr & 3)] =
+                                app_sigma;
+                }
+            }
+            Dk::read(c, m, lb, sb, kofs, vofs, g);
+            if constexpr (KV == KV_FP16)
+                if (patch && g == (tr >> 2)) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (e == 4 * tpg + (tr & 3)) c.v16[e] = app_v;
+                }
+            process_chunk<KV, NW, MQ>(st, c, qop, cscale, tok0 + 32 * ch, tok1, lo1, lim1, g);
+        };
+        typename Dk::Meta ma, mb;
         issue(ma, 0, 0);
         for (int k = 0; k < segn; k += 2) {
             if (k + 1 < segn) {
@@ -684,8 +732,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
             } else {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
-            Dk::read(c, ma, &s_dma[wave][0][0], &s_scl[KV == KV_INT8 ? wave : 0][0][0], kofs, vofs, g);
-            process_chunk<KV, NW, MQ>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k) * NW), tok1, lo1, lim1, g);
+            consume(ma, 0, k);
             if (k + 1 >= segn) break;
             if (k + 2 < segn) {
                 issue(ma, 0, k + 2);
@@ -693,9 +740,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
             } else {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
-            Dk::read(c, mb, &s_dma[wave][1][0], &s_scl[KV == KV_INT8 ? wave : 0][1][0], kofs, vofs, g);
-            process_chunk<KV, NW, MQ>(st, c, qop, cscale, tok0 + 32 * (cw + (seg + k + 1) * NW), tok1, lo1, lim1,
-                                      g);
+            consume(mb, 1, k + 1);
         }
     }
     __syncthreads();                                   // the merge below reuses the DMA buffers
@@ -1483,7 +1528,16 @@ hipError_t launch_decode_partials(const DecodeParams& p0, hipStream_t s) {
     // sequence's partitions together.
     DecodeParams p = p0;
     const int64_t units = (int64_t)p.num_seqs * p.kv.num_kv_heads;
-    p.xcd_local = p.kv.head_dim == 128 && ((units + 7) / 8) * 8 * p.ncg * p.nparts <= 256;
+    const int64_t slots = ((units + 7) / 8) * 8 * p.ncg;
+    // A fused step whose grid would leave half the compute units idle streams
+    // each partition with two workgroups (each a half of P, both merged with
+    // the rest by the LSE merge), when the workspace holds their partials.
+    if (p.kv.head_dim == 128 && p.counters && p.may_split && slots * p.nparts * 2 <= 256 &&
+        p.partition_tokens % 64 == 0 && p.partition_tokens >= 512) {
+        p.partition_tokens /= 2;
+        p.nparts *= 2;
+    }
+    p.xcd_local = p.kv.head_dim == 128 && slots * p.nparts <= 256;
     if (p.kv.head_dim == 256) {
         switch (p.kv.dtype) {
         case KV_FP16: return launch_d256<KV_FP16>(p, s);

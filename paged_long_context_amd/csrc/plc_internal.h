@@ -61,6 +61,10 @@ struct DecodeParams {
     // set by the launcher: one-dimensional grid that keeps each group's
     // partitions on one XCD (used when the whole grid is resident at once)
     int32_t xcd_local;
+    // set by the caller: the workspace holds partials for twice nparts, so
+    // the launcher may stream each partition with two workgroups (halves)
+    // when a fused-merge grid would otherwise leave compute units idle
+    int32_t may_split;
 };
 
 hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s);

@@ -109,10 +109,13 @@ def test_null_query_refused(plc):
 def test_workspace_size_formula(plc):
     # the fixed counter region, then rows * nparts * D floats and rows *
     # nparts floats, each 256-byte aligned
-    rows, nparts = 8 * 8, 16
-    want = ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
-    want += 65536
-    assert plc.decode_workspace_size(8, 8, 128, 32768, 2048) == want
+    def want(rows, nparts):
+        return ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256 + 65536
+    # 8 sequences x 16 partitions fill half the chip: room for each partition
+    # split over two workgroups (32 partials per row)
+    assert plc.decode_workspace_size(8, 8, 128, 32768, 2048) == want(8 * 8, 32)
+    # 32 sequences x 16 partitions already fill it: no split, 16 per row
+    assert plc.decode_workspace_size(32, 8, 128, 32768, 2048) == want(32 * 8, 16)
 
 
 def test_default_partition_choice(plc):
@@ -164,6 +167,7 @@ def test_verify_workspace_size_formula(plc):
     rows, nparts = 8 * 4 * 8, 16
     want = ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
     want += 65536                                                    # counter region
+    # 8 units x 2 row groups x 16 partitions = 256 workgroups: no split
     assert plc.verify_workspace_size(8, 32, 8, 1, 128, 4, 32768, 2048) == want
     assert plc.verify_workspace_size(8, 32, 8, 1, 128, 0, 32768, 2048) == 0
     assert plc.verify_workspace_size(8, 32, 8, 1, 128, 17, 32768, 2048) == 0

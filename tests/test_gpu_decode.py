@@ -60,10 +60,13 @@ def test_decode_partials_then_merge_equals_decode(plc):
     op, lp = plc.attn_decode_partials(dev(w.q), cache, bt, dev(w.context_lens), 3000, 512, sm_scale())
     o2, l2 = plc.lse_merge(op, lp)
     torch.cuda.synchronize()
-    # the fused merge and the standalone one add the parts in different
-    # (fixed) groupings: equal to fp32 rounding
-    assert np.abs(host(o2).reshape(o1.shape) - o1).max() <= 1e-6
+    # the fused step may stream each partition with two workgroups (halves)
+    # and merges in its own fixed grouping: equal up to fp32 rounding of the
+    # different groupings, and both within the parity bar of the oracle
+    assert np.abs(host(o2).reshape(o1.shape) - o1).max() <= 1e-4
     assert np.abs(host(l2).reshape(l1.shape) - l1).max() <= 1e-5
+    ro_all, rl_all = oracle_decode(w, "e4m3")
+    assert_close(host(o2), host(l2), ro_all, rl_all, what="partials + lse_merge")
     # each partial against the oracle over its key window
     c = cases.oracle_cache(w, "e4m3")
     opn, lpn = host(op), host(lp)
