@@ -5,9 +5,10 @@ Headline step (the workload the metric is quoted on): a decode step of a batch
 of 8 sequences with 32,768-token contexts, 8 query heads over 1 KV head,
 head_dim 128, E4M3 KV with fp32 per-head scales, 16-token pages scattered by a
 seeded permutation, split-KV partitions of 2,048 tokens merged by log-sum-exp.
-One step = one launch of the decode kernel, which appends the step's new K/V
-token per sequence, runs every split-KV partition and merges the partials in
-the last workgroup of each (sequence, KV head).  Eight copies of the cache
+One step = the decode kernel, which appends the step's new K/V token per
+sequence and runs every split-KV partition (1,024-token halves of the 2,048
+partitions, two workgroups each, to fill the chip), then the LSE merge kernel
+over the partials.  Eight copies of the cache
 (537 MB, twice the 256 MB Infinity Cache) are rotated so every step reads its
 keys from HBM.  Steps are captured in a HIP graph and replayed, so host launch
 overhead is not timed.
@@ -426,7 +427,6 @@ class DecodeCase:
         self.max_ctx = int(w.context_lens.max())
         self.partition = plc.decode_partition_tokens(s.num_seqs, s.num_kv_heads, self.max_ctx,
                                                      partition)
-        # zero-filled: the fused merge's completion counters start at zero
         self.ws = torch.zeros(plc.decode_workspace_size(s.num_seqs, s.num_q_heads, s.head_dim,
                                                         self.max_ctx, self.partition),
                               dtype=torch.uint8, device="cuda")
@@ -451,7 +451,7 @@ class DecodeCase:
                                    workspace=self.ws)
 
     def step(self, i):
-        """One decode step in one launch: append the step's token, attend, merge."""
+        """One decode step: append the step's token and attend (one kernel), merge."""
         self.plc.attn_decode_append(self.q, self.k_new, self.v_new, self.caches[i % len(self.caches)],
                                     self.bt, self.ctx, self.max_ctx, self.partition, self.sm,
                                     out=self.out, lse=self.lse, workspace=self.ws)
@@ -543,7 +543,7 @@ def bench_c1(plc, synthetic, cpu):
     torch.cuda.synchronize()
     st, _ = timed(run, 50e-6, smi=False)
     res = {"workload": "c1: prefill 512 tokens (append + attention), then one decode step over 513 "
-                       "(append + attention, one launch); 8 q / 1 kv, E4M3",
+                       "(append fused into the attention kernel); 8 q / 1 kv, E4M3",
            "timing": st, "note": "launch-bound correctness workload; no roofline"}
     if cpu:
         import oracle
@@ -600,7 +600,8 @@ def bench_c2(plc, synthetic, specs, args):
         "config": {
             "workload": "c2 decode: 8 seqs x 32768-token context, 8 q / 1 kv heads, head_dim 128, "
                         "E4M3 KV (fp32 per-head scales), 16-token pages, split-KV partitions of "
-                        "2048 + LSE merge; step = append 1 token/seq + decode, one launch",
+                        "2048 + LSE merge; step = append 1 token/seq fused into the partition kernel, then "
+                        "the merge kernel",
             "kv_dtype": "e4m3", "batch": 8, "context": 32768, "num_q_heads": 8,
             "num_kv_heads": 1, "head_dim": 128, "block_size": 16, "partition_tokens": 2048,
             "cache_copies_rotated": args.copies, "timing": "HIP graph replay of --steps steps, host clock",

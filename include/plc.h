@@ -35,7 +35,10 @@
  *    from 1 to 16.  There the decode family (plc_attn_decode_partials,
  *    plc_attn_decode_paged, plc_attn_decode_append, plc_attn_verify_paged,
  *    plc_attn_window_paged) writes partials and merges them in a second
- *    kernel (the one of plc_lse_merge), so the workspace counters are unused.
+ *    kernel (the one of plc_lse_merge), as it does at head_dim 128.
+ *  - fp32 outputs `out` of the decode family and every workspace start on a
+ *    16-byte boundary (PLC_ERR_INVALID_ARG otherwise; any hipMalloc'ed
+ *    buffer does).
  */
 #ifndef PLC_H
 #define PLC_H
@@ -47,21 +50,18 @@
 extern "C" {
 #endif
 
-#define PLC_ABI_VERSION 2u
+#define PLC_ABI_VERSION 3u
 
 /*
  * Every decode-family workspace (plc_attn_decode_paged / _append / _partials,
- * plc_attn_verify_paged, plc_attn_window_paged) starts with a fixed region of
- * PLC_WS_COUNTER_BYTES holding the int32 completion counters of the fused
- * merge, one per (sequence, KV head, row group), at most
- * PLC_WS_COUNTER_BYTES / 4 of them per call (more: PLC_ERR_UNSUPPORTED).  The
- * region must be zero before the first call that uses the buffer (a
- * zero-filled allocation is); every call that completes leaves it zero, so
- * one buffer may serve calls of any shape in turn.  Partial outputs fp32
- * [rows][nparts][head_dim] follow at offset PLC_WS_COUNTER_BYTES, then partial
- * LSEs fp32 [rows][nparts], each region 256-byte aligned.
+ * plc_attn_verify_paged, plc_attn_window_paged) holds the partial outputs fp32
+ * [rows][nparts][head_dim] at offset 0, then the partial LSEs fp32
+ * [rows][nparts] at the next 256-byte boundary.  Its contents need no
+ * initialization and are scratch between calls; calls that share a
+ * workspace must not overlap in time.  The merged calls run two kernels on
+ * `stream`: the partitions, then the merge of plc_lse_merge, which the kernel
+ * boundary orders after every partial is written.
  */
-#define PLC_WS_COUNTER_BYTES 65536
 
 /* KV storage types. */
 #define PLC_KV_FP16 0 /* fp16 values as is */
@@ -157,11 +157,12 @@ int plc_attn_prefill_paged(const void* q, int32_t num_q_heads, const plc_kv_cach
                            void* stream);
 
 /*
- * Workspace bytes plc_attn_decode_paged / _append / _partials need: the
- * counter region (PLC_WS_COUNTER_BYTES), partial outputs fp32
- * [num_seqs * num_q_heads][nparts][head_dim] and partial LSEs fp32
- * [num_seqs * num_q_heads][nparts] (nparts = ceil(max_context_len /
- * partition)), each region 256-byte aligned.
+ * Workspace bytes plc_attn_decode_paged / _append / _partials need: partial
+ * outputs fp32 [num_seqs * num_q_heads][nparts][head_dim] and partial LSEs
+ * fp32 [num_seqs * num_q_heads][nparts] (nparts = ceil(max_context_len /
+ * partition); twice that when the grid would fit in half the chip, which
+ * then streams each partition with two workgroups), each region 256-byte
+ * aligned.
  * partition_tokens = 0 picks the default partition for max_context_len
  * (plc_decode_partition_tokens).
  */
@@ -182,12 +183,11 @@ int32_t plc_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
  *      partitions start at multiples of it; 0 = default.
  *  out (device): fp32 [num_seqs][num_q_heads][head_dim]; lse (device): fp32
  *      [num_seqs][num_q_heads].  A sequence of length 0 gives out 0, lse -inf.
- *  workspace (device): at least plc_decode_workspace_size(...) bytes.  Its
- *      counter region must be zero before the first call that uses it (a
- *      zero-filled allocation does); every call leaves it zero again.  Calls
+ *  workspace (device): at least plc_decode_workspace_size(...) bytes.  Calls
  *      that share a workspace must not overlap in time.
- * One kernel: each partition writes its partial state, and the last partition
- * of each (sequence, KV head) to finish merges them into out / lse.
+ * Two kernels: each partition writes its partial state, then the merge
+ * combines them into out / lse.  With a single partition per sequence the
+ * partition kernel writes out / lse itself and no merge runs.
  */
 int plc_attn_decode_paged(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
                           const int32_t* block_tables, int32_t max_blocks,
@@ -197,7 +197,8 @@ int plc_attn_decode_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
                           void* stream);
 
 /*
- * One decode step in one launch: append each sequence's step token and attend.
+ * One decode step: append each sequence's step token and attend, the append
+ * fused into the partition kernel.
  * Same result, bit for bit, as plc_kv_append_quant of k_new / v_new at
  * position context_lens[b] - 1 (one token per sequence) followed by
  * plc_attn_decode_paged with the same arguments.
@@ -221,14 +222,13 @@ int plc_attn_decode_append(const void* q, const void* k_new, const void* v_new,
  * hipMalloc): the same arguments and results without a workspace.  The
  * library's own device scratch of PLC_NOALLOC_SCRATCH_BYTES stands in for it
  * (held by every device the library runs on until the process ends); its
- * address is looked up, and its counter region cleared by a kernel on
- * `stream`, on the first call on each device.  The call allocates nothing.
+ * address is looked up on the first call on each device.  The call allocates
+ * nothing, and the scratch needs no initialization.
  *  A call that needs more than PLC_NOALLOC_SCRATCH_BYTES
  *      (plc_decode_workspace_size > it) returns PLC_ERR_WORKSPACE.
  *  Every call on one device shares that device's scratch: calls that overlap
  *      in time on one device (other streams, other threads) race and give
- *      wrong results; serialize them.  Each completed call leaves the counter
- *      region zero for the next.
+ *      wrong results; serialize them.
  */
 #define PLC_NOALLOC_SCRATCH_BYTES (16 << 20)
 int plc_attn_decode_append_noalloc(const void* q, const void* k_new, const void* v_new,
@@ -247,7 +247,7 @@ int plc_attn_decode_append_noalloc(const void* q, const void* k_new, const void*
  * [0, max_q_len], already appended as its last n_b positions; row j of b
  * attends causally to keys 0 .. context_lens[b] - n_b + j (the chunked-prefill
  * rule of plc_attn_prefill_paged), computed split-KV over partition_tokens
- * and merged in the same launch as plc_attn_decode_paged does.  With n_b = 1
+ * and merged as plc_attn_decode_paged does.  With n_b = 1
  * for every b it computes what plc_attn_decode_paged computes.
  *  q (device): fp16 [total_q_tokens][num_q_heads][head_dim], sequence b's
  *      tokens at rows cu_q_lens[b] ..; out fp32 [total_q_tokens][num_q_heads]
@@ -257,8 +257,7 @@ int plc_attn_decode_append_noalloc(const void* q, const void* k_new, const void*
  *  max_q_len (host): bound on every n_b, 1 .. PLC_VERIFY_MAX_Q_LEN (larger
  *      counts are a prefill: PLC_ERR_INVALID_ARG); n_b above it is clamped.
  *  partition_tokens: as for plc_attn_decode_paged (0 = automatic).
- *  workspace: plc_verify_workspace_size bytes, zero-filled before its first
- *      use; the call leaves its counters zero again.
+ *  workspace: plc_verify_workspace_size bytes.
  * A row whose causal range holds no key (n_b > context_lens[b]) gets out 0
  * and lse -inf.  Calls that share a workspace must not overlap.
  */
@@ -288,7 +287,7 @@ int plc_attn_verify_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
  * 0: no window, which is plc_attn_verify_paged).  Only the partitions that
  * hold a row's window are computed, so the cost follows the window, not the
  * context; the automatic partition size follows the window too.
- *  workspace: plc_window_workspace_size bytes, zero-filled before first use.
+ *  workspace: plc_window_workspace_size bytes.
  */
 size_t plc_window_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
@@ -304,11 +303,9 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
 /*
  * First half of plc_attn_decode_paged: per-partition normalized outputs and
  * LSEs into the workspace, laid out as plc_lse_merge reads them (o_parts at
- * offset PLC_WS_COUNTER_BYTES, lse_parts at *lse_parts_offset bytes, nparts
- * in *nparts).
+ * offset 0, lse_parts at *lse_parts_offset bytes, nparts in *nparts).
  * Partitions past a sequence's end hold o = 0, lse = -inf.  Lets a caller
  * merge partials from several sources (e.g. key shards on other devices).
- * Does not touch the workspace's counters.
  */
 int plc_attn_decode_partials(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
                              const int32_t* block_tables, int32_t max_blocks,

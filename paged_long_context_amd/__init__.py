@@ -24,8 +24,7 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libplc.so")
-ABI_VERSION = 2
-WS_COUNTER_BYTES = 65536   # PLC_WS_COUNTER_BYTES: the counter region at the workspace start
+ABI_VERSION = 3
 
 KV_FP16, KV_E4M3, KV_INT8 = 0, 1, 2
 DTYPE_CODES = {"fp16": KV_FP16, "e4m3": KV_E4M3, "int8": KV_INT8}
@@ -244,8 +243,7 @@ def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, part
 def _workspace(q, num_seqs, Hq, D, max_context_len, partition_tokens, workspace):
     need = decode_workspace_size(num_seqs, Hq, D, max_context_len, partition_tokens)
     if workspace is None:
-        # zero-filled: the fused merge's completion counters start at zero
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8)
     return workspace
 
@@ -283,7 +281,7 @@ def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor
                        partition_tokens: int = 0, sm_scale: Optional[float] = None, out=None,
                        lse=None, workspace=None, stream=None):
     """Append each sequence's step token (k_new / v_new fp16 [B][Hkv][D], at
-    position context_lens - 1) and decode, in one launch."""
+    position context_lens - 1) and decode; the append runs inside the partition kernel."""
     B, Hq, D = q.shape
     _need(q, "q", torch.float16)
     _need(k_new, "k_new", torch.float16, (B, cache.num_kv_heads, D))
@@ -362,7 +360,7 @@ def attn_decode_partials(q: torch.Tensor, cache: KVCache, block_tables: torch.Te
                                          ctypes.byref(nparts), ctypes.byref(off), _stream(stream)))
     n = nparts.value
     rows = B * Hq
-    o = workspace[WS_COUNTER_BYTES: WS_COUNTER_BYTES + rows * n * D * 4].view(torch.float32).view(rows, n, D)
+    o = workspace[: rows * n * D * 4].view(torch.float32).view(rows, n, D)
     l = workspace[off.value: off.value + rows * n * 4].view(torch.float32).view(rows, n)
     return o, l
 
@@ -424,8 +422,7 @@ def attn_window_paged(q: torch.Tensor, cache: KVCache, block_tables: torch.Tenso
     if workspace is None:
         need = window_workspace_size(B, T, Hq, cache.num_kv_heads, D, int(max_q_len),
                                      int(max_context_len), int(window_tokens), int(partition_tokens))
-        # zero-filled: the merge's completion counters start at zero
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)

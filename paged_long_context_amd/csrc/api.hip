@@ -16,7 +16,7 @@
 #include "plc_internal.h"
 
 // Device scratch of plc_attn_decode_append_noalloc: the decode workspace
-// (counter region, partial outputs, partial LSEs) for callers that cannot
+// (partial outputs, partial LSEs) for callers that cannot
 // allocate one.  Every device the library runs on holds its own copy until
 // the process ends.  In host code this name is only a handle for
 // hipGetSymbolAddress; kernels get the device address it returns.
@@ -110,24 +110,20 @@ int hip_status(hipError_t e, const char* what) {
     return PLC_OK;
 }
 
-// Workspace layout of the decode family: the completion counters of the
-// fused merge in a fixed region at offset 0 (so a workspace reused for calls
-// of other shapes keeps them where every call expects them, zero), then the
-// partial outputs and the partial LSEs.
+// Workspace layout of the decode family: the partial outputs, then the
+// partial LSEs.
 void set_workspace(plc::DecodeParams* p, void* ws, size_t rows, int32_t nparts, int32_t head_dim) {
     char* base = static_cast<char*>(ws);
     const size_t o_bytes = align_up(rows * nparts * head_dim * sizeof(float));
-    p->counters = reinterpret_cast<int32_t*>(base);
-    p->o_parts = reinterpret_cast<float*>(base + PLC_WS_COUNTER_BYTES);
-    p->lse_parts = reinterpret_cast<float*>(base + PLC_WS_COUNTER_BYTES + o_bytes);
+    p->o_parts = reinterpret_cast<float*>(base);
+    p->lse_parts = reinterpret_cast<float*>(base + o_bytes);
 }
 
 size_t partial_bytes(size_t rows, int64_t nparts, int32_t head_dim) {
-    return PLC_WS_COUNTER_BYTES + align_up(rows * nparts * head_dim * sizeof(float)) +
-           align_up(rows * nparts * sizeof(float));
+    return align_up(rows * nparts * head_dim * sizeof(float)) + align_up(rows * nparts * sizeof(float));
 }
 
-// A fused-merge launch of at most this many workgroup slots (rounded units of
+// A merged launch of at most this many workgroup slots (rounded units of
 // eight (sequence, KV head) groups x row groups x partitions) leaves compute
 // units idle on the 256-CU chip; the launcher then streams each partition
 // with two workgroups, and the workspace holds partials for 2 nparts.
@@ -144,11 +140,10 @@ size_t decode_partial_bytes(size_t rows, int64_t units, int32_t ncg, int64_t npa
     return partial_bytes(rows, split ? 2 * nparts : nparts, head_dim);
 }
 
-int check_groups(int64_t groups) {
-    if (groups > PLC_WS_COUNTER_BYTES / 4)
-        return fail(PLC_ERR_UNSUPPORTED,
-                    "%lld (sequence, KV head, row group) merge groups: at most %d per call",
-                    (long long)groups, PLC_WS_COUNTER_BYTES / 4);
+// the kernels store 16-byte vectors to out and the workspace
+int check_aligned(const void* ptr, const char* what) {
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+        return fail(PLC_ERR_INVALID_ARG, "%s at %p is not 16-byte aligned", what, ptr);
     return PLC_OK;
 }
 
@@ -179,13 +174,13 @@ int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
                     partition_tokens, kv->block_size);
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
         return fail(PLC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
-    if ((rc = check_groups((int64_t)num_seqs * kv->num_kv_heads))) return rc;
     const int32_t P = resolve_partition(num_seqs, kv->num_kv_heads, max_context_len, partition_tokens);
     const size_t need = plc_decode_workspace_size(num_seqs, num_q_heads, kv->head_dim,
                                                   max_context_len, P);
     if (!workspace || workspace_bytes < need)
         return fail(PLC_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
                     workspace_bytes, workspace, need);
+    if ((rc = check_aligned(workspace, "workspace"))) return rc;
     const int32_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
     const size_t rows = (size_t)num_seqs * num_q_heads;
     plc::DecodeParams& p = *out;
@@ -203,6 +198,9 @@ int decode_setup(const void* q, int32_t num_q_heads, const plc_kv_cache* kv,
     set_workspace(&p, workspace, rows, nparts, kv->head_dim);
     p.may_split = workspace_bytes >= partial_bytes(rows, 2 * (int64_t)nparts, kv->head_dim) ? 1 : 0;
     if (p.may_split) set_workspace(&p, workspace, rows, 2 * nparts, kv->head_dim);
+    p.merge = 0;
+    p.direct = 0;
+    p.xcd_local = 0;
     p.out = nullptr;
     p.lse = nullptr;
     p.k_new = nullptr;
@@ -236,14 +234,13 @@ void mq_partitions(int32_t groups, int32_t num_kv_heads, int32_t max_q_len, int3
     if (*nparts < 1) *nparts = 1;
 }
 
-// Per-device address of `scratch`, looked up (and its counter region
-// cleared by a kernel on the caller's stream) on the first call on each
+// Per-device address of `scratch`, looked up on the first call on each
 // device, with that device current.
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-int scratch_for_current_device(hipStream_t s, void** out) {
+int scratch_for_current_device(void** out) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_status(e, "hipGetDevice");
@@ -256,8 +253,6 @@ int scratch_for_current_device(hipStream_t s, void** out) {
         e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
         if (e != hipSuccess || !ptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
                                                        "hipGetSymbolAddress(scratch)");
-        e = plc::launch_fill_zero(ptr, PLC_WS_COUNTER_BYTES, s);
-        if (e != hipSuccess) return hip_status(e, "clearing the scratch counters");
         g_scratch_ptr[dev] = ptr;
     }
     *out = g_scratch_ptr[dev];
@@ -356,7 +351,7 @@ size_t plc_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
                           : resolve_partition(num_seqs, 1, max_context_len, 0);
     const int64_t nparts = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
     const size_t rows = (size_t)num_seqs * num_q_heads;
-    // the counter region, partial outputs and partial LSEs; sized for one KV
+    // partial outputs and partial LSEs; sized for one KV
     // head (the fewest units, so the split partitions whenever they may occur)
     return decode_partial_bytes(rows, num_seqs, 1, nparts, P, head_dim);
 }
@@ -374,7 +369,6 @@ int plc_attn_decode_partials(const void* q, int32_t num_q_heads, const plc_kv_ca
     if (nparts) *nparts = p.nparts;
     if (lse_parts_offset)
         *lse_parts_offset = (size_t)(reinterpret_cast<char*>(p.lse_parts) - static_cast<char*>(workspace));
-    p.counters = nullptr;                              // partials only: no merge
     return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)),
                       "decode partition launch");
 }
@@ -389,7 +383,9 @@ int plc_attn_decode_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
                           max_context_len, partition_tokens, sm_scale, workspace, workspace_bytes, &p);
     if (rc) return rc;
     if (!out || !lse) return fail(PLC_ERR_INVALID_ARG, "out / lse is NULL");
-    p.out = out;                                       // the last partition of each group merges
+    if ((rc = check_aligned(out, "out"))) return rc;
+    p.merge = 1;
+    p.out = out;
     p.lse = lse;
     return hip_status(plc::launch_decode_partials(p, static_cast<hipStream_t>(stream)),
                       "decode launch");
@@ -407,6 +403,8 @@ int plc_attn_decode_append(const void* q, const void* k_new, const void* v_new,
     if (rc) return rc;
     if (!out || !lse) return fail(PLC_ERR_INVALID_ARG, "out / lse is NULL");
     if (!k_new || !v_new) return fail(PLC_ERR_INVALID_ARG, "k_new / v_new is NULL");
+    if ((rc = check_aligned(out, "out"))) return rc;
+    p.merge = 1;
     p.out = out;
     p.lse = lse;
     p.k_new = k_new;
@@ -432,7 +430,7 @@ int plc_attn_decode_append_noalloc(const void* q, const void* k_new, const void*
                     "(use plc_attn_decode_append with a workspace)",
                     need, PLC_NOALLOC_SCRATCH_BYTES);
     void* ws = nullptr;
-    const int rc = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws);
+    const int rc = scratch_for_current_device(&ws);
     if (rc) return rc;
     return plc_attn_decode_append(q, k_new, v_new, num_q_heads, kv, block_tables, max_blocks, context_lens,
                                   num_seqs, max_context_len, partition_tokens, sm_scale, out, lse, ws,
@@ -453,7 +451,6 @@ size_t plc_window_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32
     mq_partitions(num_seqs * ncg, num_kv_heads, max_q_len, max_context_len, window_tokens,
                   partition_tokens, &P, &nparts);
     const size_t rows = (size_t)total_q_tokens * num_q_heads;
-    // the counter region (one counter per (sequence, KV head, row group)),
     // partial outputs and LSEs per query row
     return decode_partial_bytes(rows, (int64_t)num_seqs * num_kv_heads, ncg, nparts, P, head_dim);
 }
@@ -494,7 +491,6 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
         return fail(PLC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
     const int32_t ncg = verify_row_groups(num_q_heads, kv->num_kv_heads, max_q_len);
-    if ((rc = check_groups((int64_t)num_seqs * kv->num_kv_heads * ncg))) return rc;
     int32_t P = 0, nparts = 0;
     mq_partitions(num_seqs * ncg, kv->num_kv_heads, max_q_len, max_context_len, window_tokens,
                   partition_tokens, &P, &nparts);
@@ -504,6 +500,7 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     if (!workspace || workspace_bytes < need)
         return fail(PLC_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
                     workspace_bytes, workspace, need);
+    if ((rc = check_aligned(workspace, "workspace")) || (rc = check_aligned(out, "out"))) return rc;
     const size_t rows = (size_t)total_q_tokens * num_q_heads;
     plc::DecodeParams p;
     p.q = q;
@@ -520,6 +517,9 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     set_workspace(&p, workspace, rows, nparts, kv->head_dim);
     p.may_split = workspace_bytes >= partial_bytes(rows, 2 * (int64_t)nparts, kv->head_dim) ? 1 : 0;
     if (p.may_split) set_workspace(&p, workspace, rows, 2 * nparts, kv->head_dim);
+    p.merge = 1;
+    p.direct = 0;
+    p.xcd_local = 0;
     p.out = out;
     p.lse = lse;
     p.k_new = nullptr;

@@ -359,119 +359,23 @@ struct RowMap {
     }
 };
 
-// Merge the partitions of one (sequence, KV head, row group); run by the
-// workgroup that finished last.  One pass over the partials, every thread holding
-// several 16-byte loads in flight: thread (sub, d4) owns columns 4*d4..+3 of
-// row j for the parts k = ks, ks + KS, ... of its subset and keeps a running
-// maximum; the subsets are then combined in a fixed order through LDS.
-// lds must hold 2 * NW * (32 * 4 + 2) floats.
-template <int NW>
-__device__ void merge_group(const DecodeParams& p, const RowMap& rm, int G, int nparts_b, int tid,
-                            float* lds) {
-    constexpr int NSUB = 64 * NW / 32;                  // 32-lane groups (one row slice each)
-    f32x4* s_acc = reinterpret_cast<f32x4*>(lds);       // [NSUB][32]
-    float* s_m = lds + NSUB * 32 * 4;                   // [NSUB]
-    float* s_w = s_m + NSUB;                            // [NSUB]
-    const int nparts = p.nparts;
-    const int sub = tid >> 5, d4 = tid & 31;
-    const int RP = G < NSUB ? G : NSUB;                  // rows per pass
-    const int KS = NSUB / RP;                            // part subsets per row
-    const float NEG = -__builtin_inff();
-    for (int j0 = 0; j0 < G; j0 += RP) {
-        const int j = j0 + sub % RP, ks = sub / RP;
-        const int64_t row = rm.row(j < G ? j : 0);       // j >= G only in a spare pass slot
-        const float* lp = p.lse_parts + row * nparts;
-        const f32x4* op = reinterpret_cast<const f32x4*>(p.o_parts + row * nparts * D) + d4;
-        f32x4 acc = f32x4{0, 0, 0, 0};
-        float m = NEG, wsum = 0.0f;                      // running max (natural log units)
-        int k = ks;
-        for (; k + 7 * KS < nparts_b; k += 8 * KS) {
-            float lk[8];
-            f32x4 ov[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                lk[u] = lp[k + u * KS];
-                ov[u] = op[(int64_t)(k + u * KS) * (D / 4)];
-            }
-            // all 16 loads in one round trip: without this the compiler sinks
-            // the partial loads into the branch below, behind the LSE loads
-#pragma unroll
-            for (int u = 0; u < 8; ++u) pin(ov[u]);
-            float mb = m;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) mb = fmaxf(mb, lk[u]);
-            if (mb != NEG) {
-                const float sc = fast_exp2((m - mb) * kLog2e);   // 0 while m is -inf
-                acc *= sc;
-                wsum *= sc;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float w = fast_exp2((lk[u] - mb) * kLog2e);
-                    wsum += w;
-                    acc += w * ov[u];
-                }
-                m = mb;
-            }
-        }
-        for (; k < nparts_b; k += KS) {
-            const float lk = lp[k];
-            const f32x4 ov = op[(int64_t)k * (D / 4)];
-            const float mb = fmaxf(m, lk);
-            if (mb != NEG) {
-                const float sc = fast_exp2((m - mb) * kLog2e);
-                const float w = fast_exp2((lk - mb) * kLog2e);
-                acc = acc * sc + w * ov;
-                wsum = wsum * sc + w;
-                m = mb;
-            }
-        }
-        s_acc[sub * 32 + d4] = acc;
-        if (d4 == 0) {
-            s_m[sub] = m;
-            s_w[sub] = wsum;
-        }
-        __syncthreads();
-        if (ks == 0 && j < G) {
-            float M = NEG;
-            for (int t = 0; t < KS; ++t) M = fmaxf(M, s_m[sub + t * RP]);
-            f32x4 a = f32x4{0, 0, 0, 0};
-            float ws = 0.0f;
-            if (M != NEG)
-                for (int t = 0; t < KS; ++t) {
-                    const int o = sub + t * RP;
-                    const float sc = fast_exp2((s_m[o] - M) * kLog2e);
-                    a += sc * s_acc[o * 32 + d4];
-                    ws += sc * s_w[o];
-                }
-            const bool empty = !(ws > 0.0f);
-            reinterpret_cast<f32x4*>(p.out + row * D)[d4] = empty ? f32x4{0, 0, 0, 0} : a / ws;
-            if (d4 == 0) p.lse[row] = empty ? NEG : M + __builtin_logf(ws);
-        }
-        __syncthreads();
-    }
-}
-
-// MQ: several query tokens per sequence (p.cu_q_lens set); without it the
-// kernel is the one-token decode, with the row map and bounds it implies
-// folded at compile time.
 template <int KV, int NW, bool MQ>
 __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     using Dk = Decode<KV, NW>;
     // Pages stream through per-wave LDS buffers (two 8 KiB chunks per wave);
-    // the wave merge and the fused merge reuse that space afterwards.
+    // the wave merge reuses that space afterwards.
     __shared__ __attribute__((aligned(16))) uint8_t s_dma[NW][2][8192];
     // INT8 per-token scales of each buffer's chunk (slots 0..15 used)
     __shared__ __attribute__((aligned(16))) f32x4 s_scl[KV == KV_INT8 ? NW : 1][2][KV == KV_INT8 ? 64 : 1];
     float* smem = reinterpret_cast<float*>(&s_dma[0][0][0]);
-    __shared__ int s_last;
     // Workgroup -> (partition, row group).  The usual grid is (partition,
     // KV head x row group, sequence).  When the whole grid fits on the chip at
     // once (p.xcd_local), it is one-dimensional instead: the hardware deals
     // workgroups to the eight XCDs in turn (i % 8), and workgroup i takes the
     // (sequence, KV head) unit 8 (i / 8 / (ncg nparts)) + i % 8, so every
-    // partition and row group of a unit runs on one XCD, beside the unit's
-    // merges; within the unit the row groups of one partition are neighbours,
-    // so the second group's page reads hit that XCD's L2.
+    // partition and row group of a unit runs on one XCD; within the unit the
+    // row groups of one partition are neighbours, so the second group's page
+    // reads hit that XCD's L2.
     int part, b, kvh, cg;
     if (p.xcd_local) {
         const int i8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
@@ -533,21 +437,15 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     int tok0 = (part + first_part) * P;
 
     if (part >= nparts_b) {                                      // partition past the end
-        if (p.counters) {
-            // fused call: only a sequence with no key at all has work here
-            if (part == 0)
-                for (int idx = tid; idx < NC * D; idx += 64 * NW) {
-                    const int64_t row = rm.row(idx / D);
-                    p.out[row * D + idx % D] = 0.0f;
-                    if (idx % D == 0) p.lse[row] = -__builtin_inff();
-                }
-            return;
-        }
+        // an empty partial (or, written directly, the output of a sequence
+        // with no key at all)
         for (int idx = tid; idx < NC * D; idx += 64 * NW) {
             const int j = idx / D, d = idx % D;
             const int64_t row = rm.row(j);
-            p.o_parts[(row * nparts + part) * D + d] = 0.0f;
-            if (d == 0) p.lse_parts[row * nparts + part] = -__builtin_inff();
+            float* od = p.direct ? p.out + row * D : p.o_parts + (row * nparts + part) * D;
+            float* ld = p.direct ? p.lse + row : p.lse_parts + row * nparts + part;
+            od[d] = 0.0f;
+            if (d == 0) *ld = -__builtin_inff();
         }
         return;
     }
@@ -768,59 +666,32 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < NC * D; idx += 64 * NW) {
-        const int j = idx / D, d = idx % D;
+    // thread t: four columns of one row per pass
+    for (int e = tid; e < NC * (D / 4); e += 64 * NW) {
+        const int j = e / (D / 4), d = 4 * (e % (D / 4));
         float M = -__builtin_inff();
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + j]);
-        float Lsum = 0.0f, O = 0.0f;
+        float Lsum = 0.0f;
+        f32x4 O = f32x4{0, 0, 0, 0};
         if (M != -__builtin_inff()) {
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 const float wt = fast_exp2(s_m[w * 16 + j] - M);
                 Lsum += s_l[w * 16 + j] * wt;
-                O += s_acc[((int64_t)w * NC + j) * AST + d] * wt;
+                O += wt * *reinterpret_cast<const f32x4*>(s_acc + ((int64_t)w * NC + j) * AST + d);
             }
         }
         const bool empty = !(Lsum > 0.0f);
-        const float ov = empty ? 0.0f : O * vscale / Lsum;
+        const f32x4 ov = O * (empty ? 0.0f : vscale / Lsum);
         const float lv = empty ? -__builtin_inff() : (M + __builtin_log2f(Lsum)) * kLn2;
         const int64_t row = rm.row(j);
-        float* od = p.o_parts + (row * nparts + part) * D + d;
-        float* ld = p.lse_parts + row * nparts + part;
-        if (p.counters) {
-            // agent-coherent (write-through) stores: another workgroup, possibly
-            // on another XCD, reads them without any L2 write-back here
-            __hip_atomic_store(od, ov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (d == 0) __hip_atomic_store(ld, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            *od = ov;
-            if (d == 0) *ld = lv;
-        }
+        // a single partition per sequence: the normalized partial is the output
+        float* od = p.direct ? p.out + row * D + d : p.o_parts + (row * nparts + part) * D + d;
+        float* ld = p.direct ? p.lse + row : p.lse_parts + row * nparts + part;
+        *reinterpret_cast<f32x4*>(od) = ov;
+        if (d == 0) *ld = lv;
     }
-    if (!p.counters) return;
-
-    // ---- fused merge: the group's last workgroup to finish combines the parts.
-    // Publication follows the scoped memory model: the barrier orders every
-    // thread's partial stores before thread 0's counter increment, an
-    // agent-scope release; the thread that sees the last count issues an
-    // agent-scope acquire before the barrier that lets its workgroup read
-    // the other workgroups' partials.  Only that workgroup pays for the
-    // cache invalidation.
-    __syncthreads();
-    if (tid == 0) {
-        int* cnt = p.counters + ((int64_t)b * p.kv.num_kv_heads + kvh) * p.ncg + cg;
-        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == nparts_b - 1);
-        if (s_last) {                                 // leave the counter zeroed for the next call
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    merge_group<NW>(p, rm, NC, nparts_b, tid, smem);
 }
 
 // ---------------------------------------------------------------- head dim 256
@@ -1165,7 +1036,7 @@ hipError_t launch_d256(const DecodeParams& p, hipStream_t s) {
     else
         hipLaunchKernelGGL((paged_decode256_kernel<KV, NW, false>), grid, dim3(64 * NW), 0, s, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !p.counters) return e;
+    if (e != hipSuccess || !p.merge) return e;
     // merged output requested: plc_lse_merge's kernel over the partials
     return launch_lse_merge(p.o_parts, p.lse_parts, p.total_q_tokens * p.num_q_heads, p.nparts, 256, p.out,
                             p.lse, s);
@@ -1173,8 +1044,8 @@ hipError_t launch_d256(const DecodeParams& p, hipStream_t s) {
 
 template <int KV, int NW, bool MQ>
 hipError_t launch_mq(const DecodeParams& p, hipStream_t s) {
-    // the wave-merge and fused-merge buffers live in the kernel's static DMA
-    // buffers (NW * 16 KiB; at most NW * (32 + 16 * 132) floats are needed)
+    // the wave-merge buffers live in the kernel's static DMA buffers
+    // (NW * 16 KiB; at most NW * (32 + 16 * 132) floats are needed)
     static_assert(NW * 16384 >= 4 * NW * (32 + 16 * (D + 4)), "merge space");
     const size_t lds = 0;
     dim3 grid(p.nparts, p.kv.num_kv_heads * p.ncg, p.num_seqs);
@@ -1182,22 +1053,18 @@ hipError_t launch_mq(const DecodeParams& p, hipStream_t s) {
         const int64_t units = (int64_t)p.num_seqs * p.kv.num_kv_heads;
         grid = dim3((unsigned)(((units + 7) / 8) * 8 * p.ncg * p.nparts), 1, 1);
     }
-    if (p.counters && !p.xcd_local) {
-        // A grid larger than the chip holds at once: the partitions, then
-        // the merge kernel.  Fused, every workgroup's agent-scope release
-        // (an L2 write-back) would be paid thousands of times per step
-        // (measured +25 us on the ragged 32-sequence step); the kernel
-        // boundary orders the partials for free.
-        DecodeParams q = p;
-        q.counters = nullptr;
-        hipLaunchKernelGGL((paged_decode_kernel<KV, NW, MQ>), grid, dim3(64 * NW), lds, s, q);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return launch_lse_merge(p.o_parts, p.lse_parts, p.total_q_tokens * p.num_q_heads, p.nparts, D, p.out,
-                                p.lse, s);
-    }
+    // The merged output: the partitions, then the merge kernel over their
+    // partials, ordered after them by the kernel boundary (no fence inside
+    // either kernel).  Measured against a merge by each group's last
+    // workgroup inside the partition kernel, the second launch is the faster
+    // one: that workgroup's agent-scope release (an L2 write-back per
+    // workgroup) and its lone reads of the group's partials cost more than
+    // the launch.
     hipLaunchKernelGGL((paged_decode_kernel<KV, NW, MQ>), grid, dim3(64 * NW), lds, s, p);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.merge || p.direct) return e;
+    return launch_lse_merge(p.o_parts, p.lse_parts, p.total_q_tokens * p.num_q_heads, p.nparts, D, p.out,
+                            p.lse, s);
 }
 
 template <int KV, int NW>
@@ -1523,21 +1390,24 @@ hipError_t launch_prefill256(const PrefillParams& p, hipStream_t s) {
 hipError_t launch_decode_partials(const DecodeParams& p0, hipStream_t s) {
     // The XCD-local placement only when every workgroup is resident at once
     // (one 128 KiB-LDS workgroup per CU, 256 CUs): then the dispatch order
-    // cannot delay any partition, and a group's partials stay on one XCD.
+    // cannot delay any partition, and the row groups of a partition share
+    // one XCD's L2.
     // Larger grids keep the sequence-major order, which starts a long
     // sequence's partitions together.
     DecodeParams p = p0;
     const int64_t units = (int64_t)p.num_seqs * p.kv.num_kv_heads;
     const int64_t slots = ((units + 7) / 8) * 8 * p.ncg;
-    // A fused step whose grid would leave half the compute units idle streams
-    // each partition with two workgroups (each a half of P, both merged with
-    // the rest by the LSE merge), when the workspace holds their partials.
-    if (p.kv.head_dim == 128 && p.counters && p.may_split && slots * p.nparts * 2 <= 256 &&
+    // A merged call whose grid would leave half the compute units idle
+    // streams each partition with two workgroups (each a half of P, both
+    // merged with the rest by the LSE merge), when the workspace holds their
+    // partials.
+    if (p.kv.head_dim == 128 && p.merge && p.may_split && slots * p.nparts * 2 <= 256 &&
         p.partition_tokens % 64 == 0 && p.partition_tokens >= 512) {
         p.partition_tokens /= 2;
         p.nparts *= 2;
     }
     p.xcd_local = p.kv.head_dim == 128 && slots * p.nparts <= 256;
+    p.direct = p.kv.head_dim == 128 && p.merge && p.nparts == 1;
     if (p.kv.head_dim == 256) {
         switch (p.kv.dtype) {
         case KV_FP16: return launch_d256<KV_FP16>(p, s);

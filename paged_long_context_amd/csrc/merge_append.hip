@@ -14,7 +14,9 @@ namespace {
 // depend on how the rows are scheduled.  Lane k of a wave computes part k's
 // weight and readlane hands it to every lane; sixteen parts' values are loaded
 // before any is used, so a row of up to sixteen parts costs one round trip.
-constexpr int kMergeWavesPerBlock = 4;
+// one wave per workgroup: a step's few hundred merge rows spread over as many
+// compute units (measured faster than four waves per workgroup)
+constexpr int kMergeWavesPerBlock = 1;
 
 __global__ __launch_bounds__(64 * kMergeWavesPerBlock) void lse_merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int rows, int nparts,
@@ -125,13 +127,6 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
     }
 }
 
-// Clears n16 16-byte words with vector stores (used where a memset node must
-// not appear in a captured graph).
-__global__ void fill_zero_kernel(u32x4* p, int64_t n16) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n16) p[i] = u32x4{0, 0, 0, 0};
-}
-
 __global__ void debug_e4m3_kernel(const uint8_t* codes, uint16_t* out, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -172,14 +167,6 @@ hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {
     case 256: return launch_kv_append_d<256>(p, s);
     default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
-    const int64_t n16 = (int64_t)(bytes / 16);
-    if (n16 == 0) return hipSuccess;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
-                       static_cast<u32x4*>(p), n16);
-    return hipGetLastError();
 }
 
 hipError_t launch_debug_e4m3(const uint8_t* codes, uint16_t* out, int32_t n, hipStream_t s) {

@@ -33,9 +33,10 @@ struct DecodeParams {
     float qk_scale_log2;        // sm_scale * log2(e)
     float* o_parts;             // [B*Hq][nparts][D]
     float* lse_parts;           // [B*Hq][nparts]
-    // fused merge (NULL counters: partials only).  counters: int32 [B][Hkv],
-    // zero on entry, left zero; out fp32 [B][Hq][D], lse fp32 [B][Hq]
-    int32_t* counters;
+    // merge != 0: the merged output is wanted in out fp32 [rows][D] and lse
+    // fp32 [rows] (the partitions, then the merge kernel over the partials);
+    // 0: partials only
+    int32_t merge;
     float* out;
     float* lse;
     // fused append of each sequence's step token (position context_len - 1):
@@ -61,9 +62,12 @@ struct DecodeParams {
     // set by the launcher: one-dimensional grid that keeps each group's
     // partitions on one XCD (used when the whole grid is resident at once)
     int32_t xcd_local;
+    // set by the launcher: merge requested and a single partition per
+    // sequence, so the partition kernel writes out and lse itself
+    int32_t direct;
     // set by the caller: the workspace holds partials for twice nparts, so
     // the launcher may stream each partition with two workgroups (halves)
-    // when a fused-merge grid would otherwise leave compute units idle
+    // when a merged call's grid would otherwise leave compute units idle
     int32_t may_split;
 };
 
@@ -107,7 +111,6 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill256(const PrefillParams& p, hipStream_t s);   // head dim 256
 
 // zero `bytes` (a multiple of 16, 16-byte aligned) with a kernel
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 hipError_t launch_debug_e4m3(const uint8_t* codes, uint16_t* out, int32_t n, hipStream_t s);
 

@@ -38,8 +38,7 @@ def test_library_exports_every_declared_symbol(plc):
 
 
 def test_abi_version(plc):
-    assert plc.lib().plc_abi_version() == plc.ABI_VERSION == 2
-    assert plc.WS_COUNTER_BYTES == 65536
+    assert plc.lib().plc_abi_version() == plc.ABI_VERSION == 3
     assert plc.verify_max_query_tokens() == plc.VERIFY_MAX_Q_LEN == 16
 
 
@@ -107,10 +106,9 @@ def test_null_query_refused(plc):
 
 
 def test_workspace_size_formula(plc):
-    # the fixed counter region, then rows * nparts * D floats and rows *
-    # nparts floats, each 256-byte aligned
+    # rows * nparts * D floats, then rows * nparts floats, each 256-byte aligned
     def want(rows, nparts):
-        return ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256 + 65536
+        return ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
     # 8 sequences x 16 partitions fill half the chip: room for each partition
     # split over two workgroups (32 partials per row)
     assert plc.decode_workspace_size(8, 8, 128, 32768, 2048) == want(8 * 8, 32)
@@ -163,10 +161,9 @@ def test_verify_validation(plc):
 
 def test_verify_workspace_size_formula(plc):
     # 8 sequences x 4 tokens x 8 heads = 256 rows, 16 partitions of 2048;
-    # 4 x 8 = 32 rows per (sequence, KV head) = 2 groups of 16 -> 16 counters
+    # 4 x 8 = 32 rows per (sequence, KV head) = 2 row groups of 16
     rows, nparts = 8 * 4 * 8, 16
     want = ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
-    want += 65536                                                    # counter region
     # 8 units x 2 row groups x 16 partitions = 256 workgroups: no split
     assert plc.verify_workspace_size(8, 32, 8, 1, 128, 4, 32768, 2048) == want
     assert plc.verify_workspace_size(8, 32, 8, 1, 128, 0, 32768, 2048) == 0
@@ -188,13 +185,14 @@ def test_head_dim_256_entry_points(plc):
     assert _decode(plc, _desc(plc, head_dim=192)) == -2 and "head_dim" in _err(plc)
 
 
-def test_too_many_merge_groups_refused(plc):
-    # one completion counter per (sequence, KV head, row group) in the fixed
-    # 64 KiB region: 16,384 groups at most per call
-    d = _desc(plc, hkv=8)
-    assert plc.lib().plc_attn_decode_paged(0x3000, 64, ctypes.byref(d), 0x4000, 4, 0x5000, 2049, 64,
-                                           0, 0.088, 0x6000, 0x7000, 0x2000, 1 << 40, None) == -2
-    assert "merge groups" in _err(plc)
+def test_misaligned_output_or_workspace_refused(plc):
+    # the kernels store 16-byte vectors into out and the workspace
+    d = _desc(plc)
+    assert _decode(plc, d, ws=0x2004) == -1 and "aligned" in _err(plc)
+    assert plc.lib().plc_attn_decode_paged(0x3000, 8, ctypes.byref(d), 0x4000, 4, 0x5000, 2, 64, 0, 0.088,
+                                           0x6008, 0x7000, 0x2000, 1 << 20, None) == -1
+    assert "out" in _err(plc) and "aligned" in _err(plc)
+    assert _verify(plc, d, ws=0x2008) == -1 and "aligned" in _err(plc)
 
 
 def test_no_alloc_refuses_more_than_its_scratch(plc):

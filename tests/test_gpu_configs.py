@@ -113,7 +113,7 @@ def test_c3_chunked_prefill_subsample(plc):
 
 
 # The call bench.py times for a decode step: plc_attn_decode_append (the
-# step's token appended inside the decode launch, fused merge) at full size
+# step's token appended inside the partition kernel, then the merge) at full size
 # in the partition bench.py resolves (2,048 for the 8 x 32K batch, automatic
 # otherwise), for every KV dtype.
 STEP_CASES = [("c2", 2048, dt) for dt in ("fp16", "e4m3", "int8")] + \

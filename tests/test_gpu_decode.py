@@ -53,6 +53,35 @@ def test_decode_group_sizes(plc, hq, hkv, dtype):
     assert_close(o, l, ro, rl, what="decode G=%d %s" % (hq // hkv, dtype))
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
+def test_decode_single_partition_writes_output_directly(plc, dtype):
+    # every context fits one 256-token partition (below the 512 the
+    # two-workgroup split needs): the partition kernel writes out / lse
+    # itself and no merge runs.  The last sequence is given length 0 on the
+    # device: out 0, lse -inf.
+    lens = [1, 17, 255, 256, 200]
+    w = synthetic.generate(cases.spec(lens, [1] * len(lens), hq=8, hkv=1, seed=207))
+    cache, bt = device_cache(plc, w, dtype)
+    ctx = w.context_lens.copy()
+    ctx[-1] = 0
+    o, l = plc.attn_decode_paged(dev(w.q), cache, bt, dev(ctx), 256, 256, sm_scale())
+    torch.cuda.synchronize()
+    o, l = host(o), host(l)
+    ro, rl = oracle_decode(w, dtype)
+    assert_close(o[:-1], l[:-1], ro[:-1], rl[:-1], what="single-partition decode %s" % dtype)
+    assert np.all(o[-1] == 0.0) and np.all(np.isneginf(l[-1]))
+
+
+def test_verify_single_partition_writes_output_directly(plc):
+    from tests.test_gpu_verify import oracle_verify, run_verify
+    ctx = [40, 256, 100, 3]
+    ql = [3, 4, 0, 3]
+    w = synthetic.generate(cases.spec(ctx, ql, hq=8, hkv=1, seed=208))
+    o, l = run_verify(plc, w, "e4m3", 256, max_q_len=4)
+    ro, rl = oracle_verify(w, "e4m3")
+    assert_close(o, l, ro, rl, what="single-partition verify")
+
+
 def test_decode_partials_then_merge_equals_decode(plc):
     w = synthetic.generate(cases.spec([3000, 900, 17], [1, 1, 1], hq=8, hkv=1, seed=203))
     cache, bt = device_cache(plc, w, "e4m3")

@@ -86,15 +86,15 @@ def test_int8_prefill_with_fp16_extreme_values(plc, d, hq, hkv):
 
 @pytest.mark.parametrize("dtype", ["e4m3", "int8"])
 def test_workspace_reused_across_shapes(plc, dtype):
-    """One zero-filled workspace serves decode, verification and decode calls
-    of different shapes and partitions in turn: the completion counters sit
-    in a fixed region that every call leaves zero."""
+    """One workspace, never initialized (filled with NaN bytes here), serves
+    decode and verification calls of different shapes and partitions in
+    turn: every call writes the partials it reads."""
     wa = synthetic.generate(cases.spec([5000, 17, 2049], [1, 1, 1], hq=8, hkv=1, seed=821))
     wb = synthetic.generate(cases.spec([900, 4100, 33, 70, 16], [3, 4, 1, 2, 2], hq=16, hkv=4,
                                        seed=822))
     ca, bta = device_cache(plc, wa, dtype)
     cb, btb = device_cache(plc, wb, dtype)
-    ws = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
+    ws = torch.full((1 << 26,), 0xFF, dtype=torch.uint8, device="cuda")
     ref_a = cases.oracle_attention(wa, cases.oracle_cache(wa, dtype), sm_scale())
     ref_b = cases.oracle_attention(wb, cases.oracle_cache(wb, dtype), sm_scale())
     for it, part in enumerate([512, 0, 48]):
@@ -105,7 +105,6 @@ def test_workspace_reused_across_shapes(plc, dtype):
         torch.cuda.synchronize()
         assert_close(host(o), host(l), *ref_a, what="decode call %d" % it)
         assert_close(host(ob), host(lb), *ref_b, what="verify call %d" % it)
-        assert int(ws[:plc.WS_COUNTER_BYTES].count_nonzero()) == 0, "counters left non-zero"
 
 
 def shard_tables(w, ranks, interleave):
