@@ -669,18 +669,26 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     // thread t: four columns of one row per pass
     for (int e = tid; e < NC * (D / 4); e += 64 * NW) {
         const int j = e / (D / 4), d = 4 * (e % (D / 4));
+        // every wave's state in one LDS round trip, then no branch
+        float mw[NW], lw[NW];
+        f32x4 aw[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            mw[w] = s_m[w * 16 + j];
+            lw[w] = s_l[w * 16 + j];
+            aw[w] = *reinterpret_cast<const f32x4*>(s_acc + (w * NC + j) * AST + d);
+        }
         float M = -__builtin_inff();
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + j]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w]);
+        const bool any = M != -__builtin_inff();
         float Lsum = 0.0f;
         f32x4 O = f32x4{0, 0, 0, 0};
-        if (M != -__builtin_inff()) {
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float wt = fast_exp2(s_m[w * 16 + j] - M);
-                Lsum += s_l[w * 16 + j] * wt;
-                O += wt * *reinterpret_cast<const f32x4*>(s_acc + ((int64_t)w * NC + j) * AST + d);
-            }
+        for (int w = 0; w < NW; ++w) {
+            const float wt = any ? fast_exp2(mw[w] - M) : 0.0f;
+            Lsum += lw[w] * wt;
+            O += wt * aw[w];
         }
         const bool empty = !(Lsum > 0.0f);
         const f32x4 ov = O * (empty ? 0.0f : vscale / Lsum);

@@ -11,12 +11,45 @@ namespace {
 // One wave per (row, 64-column slice); lane l owns column 64 * slice + l.
 // Parts are visited in index order (1Cat-vLLM README, Layer 2 "Split-KV3": the
 // fp32 partial states of the partitions are combined), so the result does not
-// depend on how the rows are scheduled.  Lane k of a wave computes part k's
-// weight and readlane hands it to every lane; sixteen parts' values are loaded
-// before any is used, so a row of up to sixteen parts costs one round trip.
+// depend on how the rows are scheduled.  Parts come in batches of up to 64:
+// lane k loads part k's LSE while every part's value of the batch is loaded
+// in the same round trip; lane k then computes part k's weight against the
+// batch maximum and readlane hands it to every lane.  A later batch (more
+// than 64 parts) rescales the running sums to its larger maximum.
 // one wave per workgroup: a step's few hundred merge rows spread over as many
 // compute units (measured faster than four waves per workgroup)
 constexpr int kMergeWavesPerBlock = 1;
+
+template <int KB>
+__device__ __forceinline__ void merge_batch(const float* lp, const float* op, int kb, int kn, int D,
+                                            int lane, float& M, float& acc, float& wsum) {
+    const float NEG = -__builtin_inff();
+    float ov[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) ov[u] = op[(int64_t)(kb + (u < kn ? u : 0)) * D];
+    const float lk = lane < kn ? lp[kb + lane] : NEG;
+    // all of the batch's loads in one round trip: without this the compiler
+    // sinks the value loads behind the LSE reduction
+#pragma unroll
+    for (int u = 0; u < KB; ++u) pin(ov[u]);
+    float mb = lk;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mb = fmaxf(mb, shfl_xor(mb, off));
+    mb = fmaxf(mb, M);
+    if (mb == NEG) return;                             // nothing visible yet
+    const float sc = (M == NEG) ? 0.0f : fast_exp2((M - mb) * kLog2e);
+    acc *= sc;
+    wsum *= sc;
+    const float wl = (lk == NEG) ? 0.0f : fast_exp2((lk - mb) * kLog2e);
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+        if (u < kn) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
+            wsum += w;
+            acc += w * ov[u];
+        }
+    M = mb;
+}
 
 __global__ __launch_bounds__(64 * kMergeWavesPerBlock) void lse_merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int rows, int nparts,
@@ -29,39 +62,13 @@ __global__ __launch_bounds__(64 * kMergeWavesPerBlock) void lse_merge_kernel(
     const int d = 64 * slice + lane;
     const bool dv = d < D;
     const float* lp = lse_parts + (int64_t)row * nparts;
-    float M = -__builtin_inff();
-    for (int k = lane; k < nparts; k += 64) M = fmaxf(M, lp[k]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
-    float acc = 0.0f, wsum = 0.0f;
-    if (M != -__builtin_inff()) {
-        const float* op = o_parts + (int64_t)row * nparts * D + (dv ? d : 0);
-        for (int kb = 0; kb < nparts; kb += 64) {
-            const int kn = min(64, nparts - kb);
-            const float lk = lane < kn ? lp[kb + lane] : -__builtin_inff();
-            const float wl = (lk == -__builtin_inff()) ? 0.0f : fast_exp2((lk - M) * kLog2e);
-            int k = 0;
-            for (; k + 16 <= kn; k += 16) {
-                float ov[16];
-#pragma unroll
-                for (int u = 0; u < 16; ++u) ov[u] = dv ? op[(int64_t)(kb + k + u) * D] : 0.0f;
-#pragma unroll
-                for (int u = 0; u < 16; ++u) pin(ov[u]);
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const float w = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k + u));
-                    wsum += w;
-                    acc += w * ov[u];
-                }
-            }
-            for (; k < kn; ++k) {
-                const float ov = dv ? op[(int64_t)(kb + k) * D] : 0.0f;
-                const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k));
-                wsum += w;
-                acc += w * ov;
-            }
-        }
+    const float* op = o_parts + (int64_t)row * nparts * D + (dv ? d : 0);
+    float M = -__builtin_inff(), acc = 0.0f, wsum = 0.0f;
+    for (int kb = 0; kb < nparts; kb += 64) {
+        const int kn = min(64, nparts - kb);
+        if (kn > 32) merge_batch<64>(lp, op, kb, kn, D, lane, M, acc, wsum);
+        else if (kn > 16) merge_batch<32>(lp, op, kb, kn, D, lane, M, acc, wsum);
+        else merge_batch<16>(lp, op, kb, kn, D, lane, M, acc, wsum);
     }
     const bool empty = !(wsum > 0.0f);
     if (dv) out[(int64_t)row * D + d] = empty ? 0.0f : acc / wsum;
