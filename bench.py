@@ -264,35 +264,43 @@ def smi_static():
     return out
 
 
-def smi_under_load(replay, max_s=8.0, warm_s=0.3):
-    """GPU clocks and power read by amd-smi while `replay` keeps the GPU busy
-    (busy for warm_s before the reading starts, so the clocks have ramped)."""
+def smi_under_load(replay, readings=3, max_s=8.0, warm_s=0.3):
+    """GPU clocks and power read by amd-smi `readings` times while `replay`
+    keeps the GPU busy (up to 16 replays queued between synchronizations, and
+    busy for warm_s before the first reading, so the clocks have ramped).
+    Returns the first reading's fields plus, per clock/power field, the list
+    of all readings."""
     n = 0
-    t_warm = time.time() + warm_s
-    while time.time() < t_warm:
-        replay()
-        n += 1
-        if n % 4 == 0:
+
+    def spin(until, p=None):
+        nonlocal n
+        while time.time() < until and (p is None or p.poll() is None):
+            replay()
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
+
+    spin(time.time() + warm_s)
+    got = []
+    for _ in range(readings):
+        try:
+            p = subprocess.Popen(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"],
+                                 stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+        except Exception as e:
             torch.cuda.synchronize()
-    try:
-        p = subprocess.Popen(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"],
-                             stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
-    except Exception as e:
-        torch.cuda.synchronize()
-        return {"error": "%s: %s" % (type(e).__name__, e)}
-    t_end = time.time() + max_s
-    while p.poll() is None and time.time() < t_end:
-        replay()
-        n += 1
-        if n % 4 == 0:
-            torch.cuda.synchronize()
+            return {"error": "%s: %s" % (type(e).__name__, e)}
+        spin(time.time() + max_s, p)
+        try:
+            out, _ = p.communicate(timeout=10)
+            got.append(smi_filter(json.loads(out)))
+        except Exception as e:
+            p.kill()
+            got.append({"error": "%s: %s" % (type(e).__name__, str(e)[:200])})
     torch.cuda.synchronize()
-    try:
-        out, _ = p.communicate(timeout=10)
-        return smi_filter(json.loads(out))
-    except Exception as e:
-        p.kill()
-        return {"error": "%s: %s" % (type(e).__name__, str(e)[:200])}
+    res = dict(got[0])
+    keys = [k for k in res if k.startswith("clock.gfx_0") or k.startswith("clock.mem_0") or k.startswith("power")]
+    res["readings"] = {k: [g.get(k) for g in got] for k in keys}
+    return res
 
 
 # ------------------------------------------------------------------ timing
@@ -411,6 +419,23 @@ def build_cache(plc, w, dtype, copies):
     return caches, bt
 
 
+def step_kernel_partition(spec, max_context_len, partition):
+    """The partition the decode step's partition kernel streams: half of
+    `partition` when the library runs each partition as two workgroups (a
+    one-token decode at head dim 128 whose grid, 8 ceil(units / 8) x nparts
+    workgroups, would fill at most half of the 256 compute units; the
+    partition a multiple of 64 and at least 512), else `partition`.  A
+    partials call at this partition launches the step's partition kernel
+    without the fused append (tests/test_gpu_decode.py checks the two give
+    bitwise-equal merged outputs)."""
+    units = spec.num_seqs * spec.num_kv_heads
+    nparts = -(-max_context_len // partition) if max_context_len > 0 else 1
+    if (spec.head_dim == 128 and ((units + 7) // 8) * 8 * nparts * 2 <= 256 and partition % 64 == 0
+            and partition >= 512):
+        return partition // 2
+    return partition
+
+
 class DecodeCase:
     """A decode workload on the device with `copies` rotated caches."""
 
@@ -435,6 +460,13 @@ class DecodeCase:
         self.lse = torch.empty((s.num_seqs, s.num_q_heads), dtype=torch.float32, device="cuda")
         self.sm = 1.0 / math.sqrt(s.head_dim)
         self.parts = None
+        self.kernel_partition = step_kernel_partition(s, self.max_ctx, self.partition)
+        self.kws = torch.empty(plc.decode_workspace_size(s.num_seqs, s.num_q_heads, s.head_dim,
+                                                         self.max_ctx, self.kernel_partition),
+                               dtype=torch.uint8, device="cuda")
+        self.mout = torch.empty((s.num_seqs * s.num_q_heads, s.head_dim), dtype=torch.float32,
+                                device="cuda")
+        self.mlse = torch.empty((s.num_seqs * s.num_q_heads,), dtype=torch.float32, device="cuda")
 
     def append(self, i):
         self.plc.kv_append_quant(self.caches[i % len(self.caches)], self.k_new, self.v_new, self.bt,
@@ -444,6 +476,16 @@ class DecodeCase:
         self.parts = self.plc.attn_decode_partials(self.q, self.caches[i % len(self.caches)], self.bt,
                                                    self.ctx, self.max_ctx, self.partition, self.sm,
                                                    workspace=self.ws)
+
+    def kernel(self, i):
+        """The step's partition kernel alone (no fused append, no merge)."""
+        self.kparts = self.plc.attn_decode_partials(self.q, self.caches[i % len(self.caches)], self.bt,
+                                                    self.ctx, self.max_ctx, self.kernel_partition,
+                                                    self.sm, workspace=self.kws)
+
+    def merge(self, i):
+        """The step's merge kernel alone, over the partials of kernel()."""
+        self.plc.lse_merge(*self.kparts, out=self.mout, lse=self.mlse)
 
     def decode(self, i):
         self.plc.attn_decode_paged(self.q, self.caches[i % len(self.caches)], self.bt, self.ctx,
@@ -574,16 +616,26 @@ def bench_c2(plc, synthetic, specs, args):
     wall, ev = head.once()
     step_bytes = decode_bytes(w2, "e4m3") + append_bytes(w2, "e4m3")
     value = step_bytes / wall / 1e9
-    achieved = step_bytes / ev / 1e9
     del head
     dist, _ = timed(c2.step, ev, smi=not args.no_breakdown)
+    # the dominant kernel: the step's partition kernel, launched alone at the
+    # partition the step streams; its algorithmic bytes are the keys, values,
+    # scales, table entries and queries it reads
+    for i in range(3):
+        c2.kernel(i)
+    kst, _ = timed(c2.kernel, ev, smi=False)
+    mst, _ = timed(c2.merge, 3e-6, smi=False)
+    kbytes = decode_bytes(w2, "e4m3", with_outputs=False)
+    achieved = kbytes / (kst["mean_us"] * 1e-6) / 1e9
     pk = two = app = None
     if not args.no_breakdown:
         pk, _ = timed(c2.partials, ev, smi=False)
         two, _ = timed(c2.step_two_launches, ev, smi=False)
         app, _ = timed(c2.append, 3e-6, smi=False)
-    log("c2 step %.2f us (events %.2f us; median %.2f, p10 %.2f, p90 %.2f) = %.0f GB/s"
-        % (wall * 1e6, ev * 1e6, dist["median_us"], dist["p10_us"], dist["p90_us"], value))
+    log("c2 step %.2f us (events %.2f us; median %.2f, p10 %.2f, p90 %.2f) = %.0f GB/s; partition kernel "
+        "%.2f us = %.0f GB/s, merge kernel %.2f us"
+        % (wall * 1e6, ev * 1e6, dist["median_us"], dist["p10_us"], dist["p90_us"], value, kst["mean_us"],
+           achieved, mst["mean_us"]))
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -610,16 +662,26 @@ def bench_c2(plc, synthetic, specs, args):
         "roofline": {
             "bound": "hbm", "kernel": DECODE_KERNEL, "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic("c2"), "bytes_per_launch": step_bytes,
-            "avg_launch_us": round(ev * 1e6, 3),
+            "traffic": read_traffic("c2"), "bytes_per_launch": kbytes,
+            "avg_launch_us": kst["mean_us"],
+            "launch": "the step's partition kernel alone (partials call at partition %d, the %d "
+                      "partitions of %d each streamed as two workgroups), graph replays of %d "
+                      "back-to-back launches between HIP events (per-launch time includes the "
+                      "launch gap)" % (c2.kernel_partition, 32768 // 2048, 2048,
+                                       kst["calls_per_sample"]),
+            "merge_kernel_avg_us": mst["mean_us"],
+            "step_avg_us_events": round(ev * 1e6, 3),
+            "step_frac_of_hbm_peak": round(step_bytes / ev / 1e9 / HBM_PEAK_GBS, 4),
         },
         "timing": dict(dist, frac_of_hbm_peak_at_median=round(step_bytes / dist["median_us"] / 1e3 /
                                                                HBM_PEAK_GBS, 4)),
     }
     if pk is not None:
-        result["step_breakdown_us"] = {"step_one_launch_median": dist["median_us"],
-                                       "partitions_only_median": pk["median_us"],
-                                       "append_then_decode_two_launches_median": two["median_us"],
+        result["step_breakdown_us"] = {"step_median": dist["median_us"],
+                                       "partition_kernel_median": kst["median_us"],
+                                       "merge_kernel_median": mst["median_us"],
+                                       "partials_at_2048_unsplit_median": pk["median_us"],
+                                       "append_then_decode_median": two["median_us"],
                                        "append_alone_median": app["median_us"]}
     return result, c2, w2, step_bytes
 
@@ -689,7 +751,10 @@ def bench_decode_config(plc, synthetic, specs, name, dtypes, cpu, w=None):
         torch.cuda.synchronize()
         one = GraphTimer(c.step, 1).once()[1]
         st, _ = timed(c.step, one)
-        kst, _ = timed(c.partials, one, smi=False)
+        for i in range(3):
+            c.kernel(i)
+        kst, _ = timed(c.kernel, one, smi=False)
+        mst, _ = timed(c.merge, 3e-6, smi=False)
         c.step(0)
         torch.cuda.synchronize()
         o_h, l_h = c.out.cpu().numpy(), c.lse.cpu().numpy()
@@ -697,18 +762,25 @@ def bench_decode_config(plc, synthetic, specs, name, dtypes, cpu, w=None):
         kb = decode_bytes(w, dt, with_outputs=False)
         med = st["median_us"] * 1e-6
         gbs = sb / med / 1e9
+        kg = kb / (kst["mean_us"] * 1e-6) / 1e9
         r = {"gbs": round(gbs, 1), "unit": "GB/s", "us_per_step": st["median_us"],
+             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+             "p10_p90_frac": [round(sb / (st["p90_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                              round(sb / (st["p10_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)],
              "partition_tokens": c.partition, "step_bytes": sb, "timing": st,
-             "partitions_only_median_us": kst["median_us"],
-             "partitions_only_gbs": round(kb / (kst["median_us"] * 1e-6) / 1e9, 1),
-             "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL, "achieved": round(gbs, 1),
-                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                          "p10_p90_frac": [round(sb / (st["p90_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                           round(sb / (st["p10_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)],
-                          "traffic": read_traffic("%s_%s" % (name, dt)), "bytes_per_launch": sb}}
-        log("%s %s: step median %.1f us (p10 %.1f, p90 %.1f) = %.0f GB/s (%.1f%%); partitions %.1f us"
+             "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL, "achieved": round(kg, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kg / HBM_PEAK_GBS, 4),
+                          "p10_p90_frac": [round(kb / (kst["p90_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                           round(kb / (kst["p10_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)],
+                          "traffic": read_traffic("%s_%s" % (name, dt)), "bytes_per_launch": kb,
+                          "avg_launch_us": kst["mean_us"],
+                          "launch": "the step's partition kernel alone (partials call at partition %d), "
+                                    "graph replays between HIP events" % c.kernel_partition,
+                          "merge_kernel_avg_us": mst["mean_us"]}}
+        log("%s %s: step median %.1f us (p10 %.1f, p90 %.1f) = %.0f GB/s (%.1f%%); partition kernel "
+            "%.1f us = %.1f%%; merge %.1f us"
             % (name, dt, st["median_us"], st["p10_us"], st["p90_us"], gbs, 100 * gbs / HBM_PEAK_GBS,
-               kst["median_us"]))
+               kst["mean_us"], 100 * kg / HBM_PEAK_GBS, mst["mean_us"]))
         del c
         torch.cuda.empty_cache()
         if cpu:

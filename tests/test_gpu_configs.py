@@ -122,7 +122,7 @@ STEP_CASES = [("c2", 2048, dt) for dt in ("fp16", "e4m3", "int8")] + \
 
 
 @pytest.mark.parametrize("name,partition,dtype", STEP_CASES)
-def test_decode_step_in_one_launch_full_size(plc, name, partition, dtype):
+def test_decode_step_full_size(plc, name, partition, dtype):
     t0 = time.time()
     w = workload(name)
     s = w.spec

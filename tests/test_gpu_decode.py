@@ -72,6 +72,25 @@ def test_decode_single_partition_writes_output_directly(plc, dtype):
     assert np.all(o[-1] == 0.0) and np.all(np.isneginf(l[-1]))
 
 
+@pytest.mark.parametrize("lens,partition", [([4096] * 8, 1024), ([32768] * 8, 2048), ([5000, 17, 2049], 256),
+                                            ([3000] * 40, 1024)])
+def test_bench_kernel_partition_is_the_steps(plc, lens, partition):
+    # bench.py times the step's partition kernel alone as a partials call at
+    # step_kernel_partition(): that call plus the merge must reproduce the
+    # merged decode bit for bit (same partitions, same arithmetic)
+    import bench
+    w = synthetic.generate(cases.spec(lens, [1] * len(lens), hq=8, hkv=1, seed=209))
+    cache, bt = device_cache(plc, w, "e4m3")
+    maxc = int(w.context_lens.max())
+    o1, l1 = run_decode(plc, w, "e4m3", partition, cache, bt)
+    kp = bench.step_kernel_partition(w.spec, maxc, partition)
+    op, lp = plc.attn_decode_partials(dev(w.q), cache, bt, dev(w.context_lens), maxc, kp, sm_scale())
+    o2, l2 = plc.lse_merge(op, lp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o2).reshape(o1.shape), o1)
+    assert np.array_equal(host(l2).reshape(l1.shape), l1)
+
+
 def test_verify_single_partition_writes_output_directly(plc):
     from tests.test_gpu_verify import oracle_verify, run_verify
     ctx = [40, 256, 100, 3]
