@@ -124,19 +124,19 @@ size_t partial_bytes(size_t rows, int64_t nparts, int32_t head_dim) {
 }
 
 // A merged launch of at most this many workgroup slots (rounded units of
-// eight (sequence, KV head) groups x row groups x partitions) leaves compute
-// units idle on the 256-CU chip; the launcher then streams each partition
-// with two workgroups, and the workspace holds partials for 2 nparts.
-bool may_split_partitions(int64_t units, int32_t ncg, int64_t nparts, int32_t partition_tokens) {
-    return ((units + 7) / 8) * 8 * ncg * nparts * 2 <= 256 && partition_tokens % 64 == 0 &&
+// eight (sequence, KV head) groups x workgroup columns x partitions) leaves
+// compute units idle on the 256-CU chip; the launcher then streams each
+// partition with two workgroups, and the workspace holds partials for 2 nparts.
+bool may_split_partitions(int64_t units, int32_t ncgw, int64_t nparts, int32_t partition_tokens) {
+    return ((units + 7) / 8) * 8 * ncgw * nparts * 2 <= 256 && partition_tokens % 64 == 0 &&
            partition_tokens >= 512;
 }
 
 // Partial bytes of a decode-family call: doubled partitions when the launch
 // may split them.
-size_t decode_partial_bytes(size_t rows, int64_t units, int32_t ncg, int64_t nparts, int32_t partition_tokens,
+size_t decode_partial_bytes(size_t rows, int64_t units, int32_t ncgw, int64_t nparts, int32_t partition_tokens,
                             int32_t head_dim) {
-    const bool split = may_split_partitions(units, ncg, nparts, partition_tokens);
+    const bool split = may_split_partitions(units, ncgw, nparts, partition_tokens);
     return partial_bytes(rows, split ? 2 * nparts : nparts, head_dim);
 }
 
@@ -452,7 +452,10 @@ size_t plc_window_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32
                   partition_tokens, &P, &nparts);
     const size_t rows = (size_t)total_q_tokens * num_q_heads;
     // partial outputs and LSEs per query row
-    return decode_partial_bytes(rows, (int64_t)num_seqs * num_kv_heads, ncg, nparts, P, head_dim);
+    // workgroup columns per (sequence, KV head): the launcher's grid
+    const int32_t rg = plc::groups_per_workgroup(head_dim, true, ncg, P);
+    return decode_partial_bytes(rows, (int64_t)num_seqs * num_kv_heads, (ncg + rg - 1) / rg, nparts, P,
+                                head_dim);
 }
 
 size_t plc_verify_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,

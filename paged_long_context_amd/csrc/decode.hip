@@ -272,15 +272,15 @@ __device__ __forceinline__ void token_ok(bool v[8], int ctok, int lo, int lim, i
     }
 }
 
-// LO: the lane's row also ignores keys below lo1 (its sliding window's start).
-template <int KV, int NW, bool LO>
-__device__ __forceinline__ void process_chunk(WaveState& st, Chunk<KV>& cur, const f16x8 qop[4],
-                                              float cscale, int ctok, int tok1, int lo1, int lim1,
-                                              int g) {
+// One chunk for RG groups of 16 query rows (lane (i, g) holds row i of each
+// group): the chunk's K and V operands are converted once and feed every
+// group's MFMAs.  LO: a lane's row also ignores keys below its lo1 (its
+// sliding window's start).
+template <int KV, int NW, bool LO, int RG>
+__device__ __forceinline__ void process_chunk(WaveState (&st)[RG], Chunk<KV>& cur, const f16x8 (&qop)[RG][4],
+                                              float cscale, int ctok, int tok1, const int (&lo1)[RG],
+                                              const int (&lim1)[RG], int g) {
     using Dk = Decode<KV, NW>;
-    // scored tokens of the lane's eight t(g, e)
-    bool ok[8];
-    token_ok<LO>(ok, ctok, lo1, lim1, cur.valid_blk, g);
     const bool partial = (ctok + 32 > tok1) || (cur.valid_blk != 3);
     if constexpr (KV != KV_FP16)
         if (partial) {
@@ -290,47 +290,56 @@ __device__ __forceinline__ void process_chunk(WaveState& st, Chunk<KV>& cur, con
         }
 
     // S^T = K Q^T per page: lane holds tokens 4g + r of page pg, head i.
-    float x[8];
+    float x[RG][8];
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
         f16x8 kop[4];
         Dk::k_operands(cur, pg, kop);
-        f32x4 s = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) s = mfma16(kop[kc], qop[kc], s);
+        for (int q = 0; q < RG; ++q) {
+            f32x4 s = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float sc = cscale;
-            if constexpr (KV == KV_INT8) sc *= cur.ks[pg][r];
-            x[4 * pg + r] = s[r] * sc;
+            for (int kc = 0; kc < 4; ++kc) s = mfma16(kop[kc], qop[q][kc], s);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float sc = cscale;
+                if constexpr (KV == KV_INT8) sc *= cur.ks[pg][r];
+                x[q][4 * pg + r] = s[r] * sc;
+            }
         }
     }
-    float mx = -__builtin_inff();
+    f16x8 pop[RG];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        x[e] = ok[e] ? x[e] : -__builtin_inff();
-        mx = fmaxf(mx, x[e]);
-    }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(st.m, mx);
-    // m_new is -inf only while every key so far is masked; keep the state finite
-    const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-    const float alpha = fast_exp2(st.m - m_use);
-    float psum = 0.0f;
-    f16x8 pop;
+    for (int q = 0; q < RG; ++q) {
+        // scored tokens of the lane's eight t(g, e)
+        bool ok[8];
+        token_ok<LO>(ok, ctok, lo1[q], lim1[q], cur.valid_blk, g);
+        float mx = -__builtin_inff();
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float pe = fast_exp2(x[e] - m_use);
-        psum += pe;
-        if constexpr (KV == KV_INT8) pe *= cur.vs[e >> 2][e & 3] * kInt8PFold;
-        pop[e] = (f16)pe;
-    }
-    st.l = st.l * alpha + psum;
-    st.m = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        for (int e = 0; e < 8; ++e) {
+            x[q][e] = ok[e] ? x[q][e] : -__builtin_inff();
+            mx = fmaxf(mx, x[q][e]);
+        }
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float m_new = fmaxf(st[q].m, mx);
+        // m_new is -inf only while every key so far is masked; keep the state finite
+        const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+        const float alpha = fast_exp2(st[q].m - m_use);
+        float psum = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) st.acc[c] *= alpha;
+        for (int e = 0; e < 8; ++e) {
+            float pe = fast_exp2(x[q][e] - m_use);
+            psum += pe;
+            if constexpr (KV == KV_INT8) pe *= cur.vs[e >> 2][e & 3] * kInt8PFold;
+            pop[q][e] = (f16)pe;
+        }
+        st[q].l = st[q].l * alpha + psum;
+        st[q].m = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st[q].acc[c] *= alpha;
+        }
     }
     f16x8 vt[8];
     Dk::v_operands(cur, vt);
@@ -344,7 +353,9 @@ __device__ __forceinline__ void process_chunk(WaveState& st, Chunk<KV>& cur, con
                 for (int e = 0; e < 8; ++e) vt[c][e] = vok[e] ? vt[c][e] : (f16)0.0f;
         }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) st.acc[c] = mfma16(vt[c], pop, st.acc[c]);
+    for (int q = 0; q < RG; ++q)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st[q].acc[c] = mfma16(vt[c], pop[q], st[q].acc[c]);
 }
 
 // Query rows of one workgroup column: column c is row r = cg16 + c of its
@@ -359,39 +370,40 @@ struct RowMap {
     }
 };
 
-template <int KV, int NW, bool MQ>
+template <int KV, int NW, bool MQ, int RG>
 __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     using Dk = Decode<KV, NW>;
+    static_assert(MQ || RG == 1, "a one-token decode has one row group");
     // Pages stream through per-wave LDS buffers (two 8 KiB chunks per wave);
     // the wave merge reuses that space afterwards.
     __shared__ __attribute__((aligned(16))) uint8_t s_dma[NW][2][8192];
     // INT8 per-token scales of each buffer's chunk (slots 0..15 used)
     __shared__ __attribute__((aligned(16))) f32x4 s_scl[KV == KV_INT8 ? NW : 1][2][KV == KV_INT8 ? 64 : 1];
     float* smem = reinterpret_cast<float*>(&s_dma[0][0][0]);
-    // Workgroup -> (partition, row group).  The usual grid is (partition,
-    // KV head x row group, sequence).  When the whole grid fits on the chip at
-    // once (p.xcd_local), it is one-dimensional instead: the hardware deals
-    // workgroups to the eight XCDs in turn (i % 8), and workgroup i takes the
-    // (sequence, KV head) unit 8 (i / 8 / (ncg nparts)) + i % 8, so every
-    // partition and row group of a unit runs on one XCD; within the unit the
-    // row groups of one partition are neighbours, so the second group's page
-    // reads hit that XCD's L2.
-    int part, b, kvh, cg;
+    // Workgroup -> (partition, workgroup column of RG row groups).  The usual
+    // grid is (partition, KV head x column, sequence).  When the whole grid
+    // fits on the chip at once (p.xcd_local), it is one-dimensional instead:
+    // the hardware deals workgroups to the eight XCDs in turn (i % 8), and
+    // workgroup i takes the (sequence, KV head) unit 8 (i / 8 / (ncgw nparts))
+    // + i % 8, so every partition and column of a unit runs on one XCD; within
+    // the unit the columns of one partition are neighbours, so the second
+    // column's page reads hit that XCD's L2.
+    int part, b, kvh, cgw;
     if (p.xcd_local) {
         const int i8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
-        const int per_unit = p.ncg * p.nparts;
+        const int per_unit = p.ncgw * p.nparts;
         const int unit = 8 * (rest / per_unit) + i8;
         if (unit >= p.num_seqs * p.kv.num_kv_heads) return;       // padding of the last eight units
         const int within = rest % per_unit;
-        part = within / p.ncg;
-        cg = within % p.ncg;
+        part = within / p.ncgw;
+        cgw = within % p.ncgw;
         kvh = unit % p.kv.num_kv_heads;
         b = unit / p.kv.num_kv_heads;
     } else {
         part = blockIdx.x;
         b = blockIdx.z;
-        kvh = MQ ? (int)blockIdx.y / p.ncg : (int)blockIdx.y;
-        cg = MQ ? (int)blockIdx.y - kvh * p.ncg : 0;
+        kvh = MQ ? (int)blockIdx.y / p.ncgw : (int)blockIdx.y;
+        cgw = MQ ? (int)blockIdx.y - kvh * p.ncgw : 0;
     }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -421,9 +433,15 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
         qa = p.cu_q_lens[b];
         n = min(max(p.cu_q_lens[b + 1] - p.cu_q_lens[b], 0), p.max_q_len);
     }
-    const RowMap rm{qa * Hq + kvh * G, Hq, 16 * cg, __builtin_ctz(G)};
-    const int NC = MQ ? min(16, n * G - 16 * cg) : G;
-    if (MQ && NC <= 0) return;                                   // no rows: no partials, no merge
+    // the column's RG row groups: group q holds rows 16 (RG cgw + q) + [0, NC[q])
+    RowMap rm[RG];
+    int NC[RG];
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+        rm[q] = RowMap{qa * Hq + kvh * G, Hq, 16 * (RG * cgw + q), __builtin_ctz(G)};
+        NC[q] = MQ ? min(16, n * G - 16 * (RG * cgw + q)) : G;
+    }
+    if (MQ && NC[0] <= 0) return;                                // no rows: no partials, no merge
     // Sliding window (MQ, p.window > 0): row j sees keys from L - n + j -
     // window + 1 on, so no row needs a key below lo_min (row 0's start); the
     // workgroups' partition index counts from the partition that holds it.
@@ -439,14 +457,16 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     if (part >= nparts_b) {                                      // partition past the end
         // an empty partial (or, written directly, the output of a sequence
         // with no key at all)
-        for (int idx = tid; idx < NC * D; idx += 64 * NW) {
-            const int j = idx / D, d = idx % D;
-            const int64_t row = rm.row(j);
-            float* od = p.direct ? p.out + row * D : p.o_parts + (row * nparts + part) * D;
-            float* ld = p.direct ? p.lse + row : p.lse_parts + row * nparts + part;
-            od[d] = 0.0f;
-            if (d == 0) *ld = -__builtin_inff();
-        }
+#pragma unroll
+        for (int q = 0; q < RG; ++q)
+            for (int idx = tid; idx < NC[q] * D; idx += 64 * NW) {
+                const int j = idx / D, d = idx % D;
+                const int64_t row = rm[q].row(j);
+                float* od = p.direct ? p.out + row * D : p.o_parts + (row * nparts + part) * D;
+                float* ld = p.direct ? p.lse + row : p.lse_parts + row * nparts + part;
+                od[d] = 0.0f;
+                if (d == 0) *ld = -__builtin_inff();
+            }
         return;
     }
     const int tok1 = min(tok0 + P, L);
@@ -515,18 +535,21 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     // Q^T operand: lane (i, g) holds row (column) i, d = 64*(kc/2) + 16g +
     // 8*(kc%2) + [0, 8); its causal limit: position L - n + j sees keys below
     // L - n + j + 1 (L for a one-token decode; nothing for a spare column).
-    f16x8 qop[4];
-    const int lim = i < NC ? L - n + 1 + ((16 * cg + i) >> rm.gshift) : 0;
-    const int lim1 = MQ ? min(lim, tok1) : tok1;       // and inside the partition
-    const int lo1 = p.window > 0 ? lim - p.window : 0;  // the row's window start (MQ)
-    {
-        const f16* q = static_cast<const f16*>(p.q) + rm.row(i < NC ? i : 0) * D;
+    f16x8 qop[RG][4];
+    int lim1[RG], lo1[RG];
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+        const bool live = i < NC[q];
+        const int lim = live ? L - n + 1 + ((rm[q].cg16 + i) >> rm[q].gshift) : 0;
+        lim1[q] = MQ ? min(lim, tok1) : tok1;         // and inside the partition
+        lo1[q] = p.window > 0 ? lim - p.window : 0;   // the row's window start (MQ)
+        const f16* qr = static_cast<const f16*>(p.q) + rm[q].row(live ? i : 0) * D;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-            if (i < NC)
-                qop[kc] = *reinterpret_cast<const f16x8*>(q + 64 * (kc >> 1) + 16 * g + 8 * (kc & 1));
+            if (live)
+                qop[q][kc] = *reinterpret_cast<const f16x8*>(qr + 64 * (kc >> 1) + 16 * g + 8 * (kc & 1));
             else
-                qop[kc] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                qop[q][kc] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
     }
     float cscale = p.qk_scale_log2;
@@ -537,11 +560,14 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
     if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
     if constexpr (KV == KV_INT8) vscale = 1.0f / kInt8PFold;
 
-    WaveState st;
-    st.m = -__builtin_inff();
-    st.l = 0.0f;
+    WaveState st[RG];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) st.acc[c] = f32x4{0, 0, 0, 0};
+    for (int q = 0; q < RG; ++q) {
+        st[q].m = -__builtin_inff();
+        st[q].l = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st[q].acc[c] = f32x4{0, 0, 0, 0};
+    }
 
     // per-lane LDS offsets of the DMA path (see Decode::issue / Decode::read)
     int dsrc[Dk::kDmaPerPage], kofs[4], vofs[4];
@@ -619,7 +645,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
                     for (int e = 0; e < 8; ++e)
                         if (e == 4 * tpg + (tr & 3)) c.v16[e] = app_v;
                 }
-            process_chunk<KV, NW, MQ>(st, c, qop, cscale, tok0 + 32 * ch, tok1, lo1, lim1, g);
+            process_chunk<KV, NW, MQ, RG>(st, c, qop, cscale, tok0 + 32 * ch, tok1, lo1, lim1, g);
         };
         typename Dk::Meta ma, mb;
         issue(ma, 0, 0);
@@ -641,64 +667,67 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeParams p) {
             consume(mb, 1, k + 1);
         }
     }
-    __syncthreads();                                   // the merge below reuses the DMA buffers
-
-    // ---- merge the waves of the workgroup (fixed order) ----
-    float l_run = st.l;
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
+    // ---- merge the waves of the workgroup (fixed order), one row group at a time ----
     constexpr int AST = D + 4;                         // padded head stride (floats)
     float* s_m = smem;                                 // [NW][16]
     float* s_l = smem + NW * 16;                       // [NW][16]
-    float* s_acc = smem + NW * 32;                     // [NW][NC][AST]
-    if (g == 0) {
-        s_m[wave * 16 + i] = st.m;
-        s_l[wave * 16 + i] = l_run;
-    }
-    if (i < NC) {
-        float* dst = s_acc + ((int64_t)wave * NC + i) * AST + 32 * g;
+    float* s_acc = smem + NW * 32;                     // [NW][16][AST]
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            f32x4 lo = f32x4{st.acc[0][r], st.acc[1][r], st.acc[2][r], st.acc[3][r]};
-            f32x4 hi = f32x4{st.acc[4][r], st.acc[5][r], st.acc[6][r], st.acc[7][r]};
-            *reinterpret_cast<f32x4*>(dst + 8 * r) = lo;
-            *reinterpret_cast<f32x4*>(dst + 8 * r + 4) = hi;
+    for (int q = 0; q < RG; ++q) {
+        __syncthreads();                               // the DMA buffers / the previous group's state
+        if (NC[q] <= 0) break;                         // uniform: no rows in this group or later ones
+        float l_run = st[q].l;
+        l_run += shfl_xor(l_run, 16);
+        l_run += shfl_xor(l_run, 32);
+        if (g == 0) {
+            s_m[wave * 16 + i] = st[q].m;
+            s_l[wave * 16 + i] = l_run;
         }
-    }
-    __syncthreads();
-    // thread t: four columns of one row per pass
-    for (int e = tid; e < NC * (D / 4); e += 64 * NW) {
-        const int j = e / (D / 4), d = 4 * (e % (D / 4));
-        // every wave's state in one LDS round trip, then no branch
-        float mw[NW], lw[NW];
-        f32x4 aw[NW];
+        if (i < NC[q]) {
+            float* dst = s_acc + ((int64_t)wave * 16 + i) * AST + 32 * g;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            mw[w] = s_m[w * 16 + j];
-            lw[w] = s_l[w * 16 + j];
-            aw[w] = *reinterpret_cast<const f32x4*>(s_acc + (w * NC + j) * AST + d);
+            for (int r = 0; r < 4; ++r) {
+                f32x4 lo = f32x4{st[q].acc[0][r], st[q].acc[1][r], st[q].acc[2][r], st[q].acc[3][r]};
+                f32x4 hi = f32x4{st[q].acc[4][r], st[q].acc[5][r], st[q].acc[6][r], st[q].acc[7][r]};
+                *reinterpret_cast<f32x4*>(dst + 8 * r) = lo;
+                *reinterpret_cast<f32x4*>(dst + 8 * r + 4) = hi;
+            }
         }
-        float M = -__builtin_inff();
+        __syncthreads();
+        // thread t: four columns of one row per pass
+        for (int e = tid; e < NC[q] * (D / 4); e += 64 * NW) {
+            const int j = e / (D / 4), d = 4 * (e % (D / 4));
+            // every wave's state in one LDS round trip, then no branch
+            float mw[NW], lw[NW];
+            f32x4 aw[NW];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w]);
-        const bool any = M != -__builtin_inff();
-        float Lsum = 0.0f;
-        f32x4 O = f32x4{0, 0, 0, 0};
+            for (int w = 0; w < NW; ++w) {
+                mw[w] = s_m[w * 16 + j];
+                lw[w] = s_l[w * 16 + j];
+                aw[w] = *reinterpret_cast<const f32x4*>(s_acc + (w * 16 + j) * AST + d);
+            }
+            float M = -__builtin_inff();
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float wt = any ? fast_exp2(mw[w] - M) : 0.0f;
-            Lsum += lw[w] * wt;
-            O += wt * aw[w];
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w]);
+            const bool any = M != -__builtin_inff();
+            float Lsum = 0.0f;
+            f32x4 O = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float wt = any ? fast_exp2(mw[w] - M) : 0.0f;
+                Lsum += lw[w] * wt;
+                O += wt * aw[w];
+            }
+            const bool empty = !(Lsum > 0.0f);
+            const f32x4 ov = O * (empty ? 0.0f : vscale / Lsum);
+            const float lv = empty ? -__builtin_inff() : (M + __builtin_log2f(Lsum)) * kLn2;
+            const int64_t row = rm[q].row(j);
+            // a single partition per sequence: the normalized partial is the output
+            float* od = p.direct ? p.out + row * D + d : p.o_parts + (row * nparts + part) * D + d;
+            float* ld = p.direct ? p.lse + row : p.lse_parts + row * nparts + part;
+            *reinterpret_cast<f32x4*>(od) = ov;
+            if (d == 0) *ld = lv;
         }
-        const bool empty = !(Lsum > 0.0f);
-        const f32x4 ov = O * (empty ? 0.0f : vscale / Lsum);
-        const float lv = empty ? -__builtin_inff() : (M + __builtin_log2f(Lsum)) * kLn2;
-        const int64_t row = rm.row(j);
-        // a single partition per sequence: the normalized partial is the output
-        float* od = p.direct ? p.out + row * D + d : p.o_parts + (row * nparts + part) * D + d;
-        float* ld = p.direct ? p.lse + row : p.lse_parts + row * nparts + part;
-        *reinterpret_cast<f32x4*>(od) = ov;
-        if (d == 0) *ld = lv;
     }
 }
 
@@ -1050,16 +1079,16 @@ hipError_t launch_d256(const DecodeParams& p, hipStream_t s) {
                             p.lse, s);
 }
 
-template <int KV, int NW, bool MQ>
+template <int KV, int NW, bool MQ, int RG>
 hipError_t launch_mq(const DecodeParams& p, hipStream_t s) {
     // the wave-merge buffers live in the kernel's static DMA buffers
     // (NW * 16 KiB; at most NW * (32 + 16 * 132) floats are needed)
     static_assert(NW * 16384 >= 4 * NW * (32 + 16 * (D + 4)), "merge space");
     const size_t lds = 0;
-    dim3 grid(p.nparts, p.kv.num_kv_heads * p.ncg, p.num_seqs);
+    dim3 grid(p.nparts, p.kv.num_kv_heads * p.ncgw, p.num_seqs);
     if (p.xcd_local) {
         const int64_t units = (int64_t)p.num_seqs * p.kv.num_kv_heads;
-        grid = dim3((unsigned)(((units + 7) / 8) * 8 * p.ncg * p.nparts), 1, 1);
+        grid = dim3((unsigned)(((units + 7) / 8) * 8 * p.ncgw * p.nparts), 1, 1);
     }
     // The merged output: the partitions, then the merge kernel over their
     // partials, ordered after them by the kernel boundary (no fence inside
@@ -1068,17 +1097,27 @@ hipError_t launch_mq(const DecodeParams& p, hipStream_t s) {
     // one: that workgroup's agent-scope release (an L2 write-back per
     // workgroup) and its lone reads of the group's partials cost more than
     // the launch.
-    hipLaunchKernelGGL((paged_decode_kernel<KV, NW, MQ>), grid, dim3(64 * NW), lds, s, p);
+    hipLaunchKernelGGL((paged_decode_kernel<KV, NW, MQ, RG>), grid, dim3(64 * NW), lds, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.merge || p.direct) return e;
     return launch_lse_merge(p.o_parts, p.lse_parts, p.total_q_tokens * p.num_q_heads, p.nparts, D, p.out,
                             p.lse, s);
 }
 
-template <int KV, int NW>
-hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
-    if (p.cu_q_lens) return launch_mq<KV, NW, true>(p, s);
-    return launch_mq<KV, NW, false>(p, s);
+// One-token decode: 4 waves for more than 8 heads per KV head, else 8.
+// Several query tokens: 8 waves, with the launcher's row groups per
+// workgroup (two per workgroup hold about 210 VGPRs, so two waves still share
+// a SIMD); FP16 keeps one group per workgroup (its operands are twice as
+// wide: two groups spill registers), 4 waves from three groups on.
+template <int KV>
+hipError_t launch_kv(const DecodeParams& p, hipStream_t s) {
+    if (!p.cu_q_lens)
+        return p.num_q_heads / p.kv.num_kv_heads > 8 ? launch_mq<KV, 4, false, 1>(p, s)
+                                                     : launch_mq<KV, 8, false, 1>(p, s);
+    if constexpr (KV == KV_FP16)
+        return p.ncg > 2 ? launch_mq<KV, 4, true, 1>(p, s) : launch_mq<KV, 8, true, 1>(p, s);
+    else
+        return p.ncgw < p.ncg ? launch_mq<KV, 8, true, 2>(p, s) : launch_mq<KV, 8, true, 1>(p, s);
 }
 
 // ---------------------------------------------------- head dim 256 prefill
@@ -1404,7 +1443,10 @@ hipError_t launch_decode_partials(const DecodeParams& p0, hipStream_t s) {
     // sequence's partitions together.
     DecodeParams p = p0;
     const int64_t units = (int64_t)p.num_seqs * p.kv.num_kv_heads;
-    const int64_t slots = ((units + 7) / 8) * 8 * p.ncg;
+    const int32_t rg = p.kv.dtype == KV_FP16 ? 1 : groups_per_workgroup(p.kv.head_dim, p.cu_q_lens != nullptr,
+                                                                          p.ncg, p.partition_tokens);
+    p.ncgw = (p.ncg + rg - 1) / rg;
+    const int64_t slots = ((units + 7) / 8) * 8 * p.ncgw;
     // A merged call whose grid would leave half the compute units idle
     // streams each partition with two workgroups (each a half of P, both
     // merged with the rest by the LSE merge), when the workspace holds their
@@ -1424,14 +1466,10 @@ hipError_t launch_decode_partials(const DecodeParams& p0, hipStream_t s) {
         default: return hipErrorInvalidValue;
         }
     }
-    // 4 waves for a one-token decode of more than 8 heads per KV head, and
-    // for a verification with more than two 16-row groups (enough workgroups
-    // to fill the chip; measured faster from 8 drafted tokens at G = 8)
-    const bool wide = p.cu_q_lens ? p.ncg > 2 : p.num_q_heads / p.kv.num_kv_heads > 8;
     switch (p.kv.dtype) {
-    case KV_FP16: return wide ? launch_t<KV_FP16, 4>(p, s) : launch_t<KV_FP16, 8>(p, s);
-    case KV_E4M3: return wide ? launch_t<KV_E4M3, 4>(p, s) : launch_t<KV_E4M3, 8>(p, s);
-    case KV_INT8: return wide ? launch_t<KV_INT8, 4>(p, s) : launch_t<KV_INT8, 8>(p, s);
+    case KV_FP16: return launch_kv<KV_FP16>(p, s);
+    case KV_E4M3: return launch_kv<KV_E4M3>(p, s);
+    case KV_INT8: return launch_kv<KV_INT8>(p, s);
     default: return hipErrorInvalidValue;
     }
 }

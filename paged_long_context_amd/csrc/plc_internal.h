@@ -59,6 +59,9 @@ struct DecodeParams {
     // query tokens in the call (rows = total_q_tokens * num_q_heads): num_seqs
     // for a one-token decode, cu_q_lens[num_seqs] with cu_q_lens
     int32_t total_q_tokens;
+    // set by the launcher: workgroup columns per (sequence, KV head), each
+    // taking groups_per_workgroup() row groups of 16
+    int32_t ncgw;
     // set by the launcher: one-dimensional grid that keeps each group's
     // partitions on one XCD (used when the whole grid is resident at once)
     int32_t xcd_local;
@@ -70,6 +73,19 @@ struct DecodeParams {
     // when a merged call's grid would otherwise leave compute units idle
     int32_t may_split;
 };
+
+// Row groups of 16 query rows that one workgroup of the 128-wide decode
+// kernel takes in a call with several query tokens per sequence (ncg groups
+// per (sequence, KV head)) and partitions of partition_tokens: two groups
+// share each converted chunk of keys and values when partitions are at least
+// 512 tokens (measured: 16 drafts over 8 x 32K, 68 -> 56 us); shorter
+// partitions (sliding windows) keep one group per workgroup, whose extra
+// workgroups hide latency.  1 for a one-token decode and at head dim 256.  An
+// FP16 cache takes one group per workgroup (wider operands: two groups spill
+// registers); sizing the workspace with this value is then conservative.
+inline int32_t groups_per_workgroup(int32_t head_dim, bool multi_token, int32_t ncg, int32_t partition_tokens) {
+    return (head_dim == 128 && multi_token && ncg >= 2 && partition_tokens >= 512) ? 2 : 1;
+}
 
 hipError_t launch_decode_partials(const DecodeParams& p, hipStream_t s);
 

@@ -161,11 +161,15 @@ def test_verify_validation(plc):
 
 def test_verify_workspace_size_formula(plc):
     # 8 sequences x 4 tokens x 8 heads = 256 rows, 16 partitions of 2048;
-    # 4 x 8 = 32 rows per (sequence, KV head) = 2 row groups of 16
-    rows, nparts = 8 * 4 * 8, 16
-    want = ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
-    # 8 units x 2 row groups x 16 partitions = 256 workgroups: no split
-    assert plc.verify_workspace_size(8, 32, 8, 1, 128, 4, 32768, 2048) == want
+    # 4 x 8 = 32 rows per (sequence, KV head) = 2 row groups of 16, which one
+    # workgroup takes together: 8 units x 16 partitions = 128 workgroups, so
+    # room for each partition streamed as two halves (32 partials per row)
+    def want(rows, nparts):
+        return ((rows * nparts * 128 * 4 + 255) // 256) * 256 + ((rows * nparts * 4 + 255) // 256) * 256
+    assert plc.verify_workspace_size(8, 32, 8, 1, 128, 4, 32768, 2048) == want(8 * 4 * 8, 32)
+    # 16 drafts: 8 row groups, two per workgroup: 8 x 4 x 16 = 512 workgroups,
+    # no split
+    assert plc.verify_workspace_size(8, 128, 8, 1, 128, 16, 32768, 2048) == want(8 * 16 * 8, 16)
     assert plc.verify_workspace_size(8, 32, 8, 1, 128, 0, 32768, 2048) == 0
     assert plc.verify_workspace_size(8, 32, 8, 1, 128, 17, 32768, 2048) == 0
 

@@ -36,7 +36,7 @@ def oracle_verify(w, dtype, rows=None):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
-@pytest.mark.parametrize("n", [2, 3, 4, 7, 16])
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 7, 10, 16])
 def test_verify_widths(plc, dtype, n):
     # contexts at and around page and partition edges; the new tokens straddle them
     ctx = [n, 17, 33, 100, 2047, 2049, 5000]
