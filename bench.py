@@ -352,10 +352,13 @@ class GraphTimer:
 
 
 def timed(fn, call_s_guess, smi=True, n=MIN_SAMPLES):
-    """Distribution of fn's per-call time: graph replays of about 200 us or
-    more each (at least one call), n of them back to back.  Returns (stats
+    """Distribution of fn's per-call time: graph replays of about 2 ms each
+    (at least one call, at most 64), n of them back to back.  The GPU waits
+    8-13 us between two replays for the next graph's launch (rocprofv3 kernel
+    traces: no gap between kernels inside a replay), so a replay holds enough
+    calls that this launch cost stays near 1 % of a call.  Returns (stats
     dict in us, GraphTimer)."""
-    steps = max(1, min(20, int(math.ceil(200e-6 / max(call_s_guess, 1e-7)))))
+    steps = max(1, min(64, int(math.ceil(2e-3 / max(call_s_guess, 1e-7)))))
     gt = GraphTimer(fn, steps)
     x = gt.samples(n) * 1e6
     st = {"median_us": round(float(np.median(x)), 3), "p10_us": round(float(np.percentile(x, 10)), 3),
