@@ -1120,319 +1120,7 @@ hipError_t launch_kv(const DecodeParams& p, hipStream_t s) {
         return p.ncgw < p.ncg ? launch_mq<KV, 8, true, 2>(p, s) : launch_mq<KV, 8, true, 1>(p, s);
 }
 
-// ---------------------------------------------------- head dim 256 prefill
-// Chunked causal prefill at head dim 256, built from the split-D decode step.
-// A workgroup takes 64 query rows of one (sequence, KV head) -- four waves of
-// 16 rows (position-major rows, so a group of six heads spans positions) --
-// and walks the keys its last row can see in 32-token chunks.  Each chunk's
-// two 128-wide halves reach one LDS buffer pair shared by the workgroup (wave
-// 0 moves half 0 and the INT8 scales, wave 1 half 1, by the decode path's
-// DMA; FP16 V rides the same DMA in the K layout), double-buffered across
-// chunks.  Every wave then runs the split-D chunk step over its own rows with
-// its lanes' causal limits and finally writes normalized rows and LSEs.  No
-// split over keys: a long prompt chunk has enough row groups to fill the chip.
-// The split-D chunk step for RG groups of 16 rows that share the chunk: the K
-// and V operands are converted once and feed every group's MFMAs.
-template <int KV, int RG>
-__device__ __forceinline__ void process_chunk_d256_rg(WaveState2 st[RG], Chunk<KV> cur[2],
-                                                      const f16x8 qop[RG][2][4], float cscale, int ctok,
-                                                      int tok1, const int lim1[RG], int g) {
-    using Dk = Decode<KV, 4, 256>;
-    bool vok[8];
-    token_ok<false>(vok, ctok, 0, tok1, cur[0].valid_blk, g);
-    const bool partial = (ctok + 32 > tok1) || (cur[0].valid_blk != 3);
-    if constexpr (KV != KV_FP16)
-        if (partial) {
-            Dk::mask_v(cur[0], vok);
-            Dk::mask_v(cur[1], vok);
-        }
-    float x[RG][8];
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-        f32x4 s[RG];
-#pragma unroll
-        for (int j = 0; j < RG; ++j) s[j] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            f16x8 kop[4];
-            Dk::k_operands(cur[h], pg, kop);
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-                for (int j = 0; j < RG; ++j) s[j] = mfma16(kop[kc], qop[j][h][kc], s[j]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float sc = cscale;
-            if constexpr (KV == KV_INT8) sc *= cur[0].ks[pg][r];
-#pragma unroll
-            for (int j = 0; j < RG; ++j) x[j][4 * pg + r] = s[j][r] * sc;
-        }
-    }
-    f16x8 pop[RG];
-#pragma unroll
-    for (int j = 0; j < RG; ++j) {
-        bool ok[8];
-        token_ok<false>(ok, ctok, 0, lim1[j], cur[0].valid_blk, g);
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            x[j][e] = ok[e] ? x[j][e] : -__builtin_inff();
-            mx = fmaxf(mx, x[j][e]);
-        }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(st[j].m, mx);
-        const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-        const float alpha = fast_exp2(st[j].m - m_use);
-        float psum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float pe = fast_exp2(x[j][e] - m_use);
-            psum += pe;
-            if constexpr (KV == KV_INT8) pe *= cur[0].vs[e >> 2][e & 3] * kInt8PFold;
-            pop[j][e] = (f16)pe;
-        }
-        st[j].l = st[j].l * alpha + psum;
-        st[j].m = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) st[j].acc[h][c] *= alpha;
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        f16x8 vt[8];
-        Dk::v_operands(cur[h], vt);
-        if constexpr (KV == KV_FP16)
-            if (partial) {
-#pragma unroll
-                for (int c = 0; c < 8; ++c)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) vt[c][e] = vok[e] ? vt[c][e] : (f16)0.0f;
-            }
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int j = 0; j < RG; ++j) st[j].acc[h][c] = mfma16(vt[c], pop[j], st[j].acc[h][c]);
-    }
-}
-
-template <int KV>
-__device__ __forceinline__ void pf256_issue(uint8_t* lbuf, f32x4* sbuf, const PrefillParams& p, int kvh, int pb0,
-                                            int pb1, bool has1, int lane, const int src[], int hoff, bool scales,
-                                            int& valid) {
-    using Dk = Decode<KV, 4, 256>;
-    valid = Dk::valid_bits(pb0, pb1, has1, p.kv.num_blocks);
-    const int Hkv = p.kv.num_kv_heads;
-    const int pbs[2] = {(valid & 1) ? pb0 : 0, (valid & 2) ? pb1 : 0};
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-        const int64_t base = ((int64_t)pbs[pg] * Hkv + kvh) * (BS * Dk::RB) + hoff;
-        const uint8_t* kp = static_cast<const uint8_t*>(p.kv.k) + base;
-        const uint8_t* vp = static_cast<const uint8_t*>(p.kv.v) + base;
-        if constexpr (KV == KV_FP16) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                Dk::dma16(kp + src[q], lbuf + 4096 * pg + 1024 * q);
-                Dk::dma16(vp + src[q], lbuf + 8192 + 4096 * pg + 1024 * q);
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                Dk::dma16(kp + src[q], lbuf + 2048 * pg + 1024 * q);
-                Dk::dma16(vp + src[q], lbuf + 4096 + 2048 * pg + 1024 * q);
-            }
-        }
-    }
-    if constexpr (KV == KV_INT8)
-        if (scales) {
-            const int sl = lane & 15, spg = (sl >> 2) & 1;
-            const float* sc = ((sl >> 3) ? p.kv.v_scale : p.kv.k_scale) + ((int64_t)pbs[spg] * Hkv + kvh) * BS +
-                              4 * (sl & 3);
-            Dk::dma16(reinterpret_cast<const uint8_t*>(sc), reinterpret_cast<uint8_t*>(sbuf));
-        }
-    (void)sbuf;
-    (void)scales;
-}
-
-template <int KV, int RG>
-__global__ __launch_bounds__(256) void paged_prefill256_kernel(PrefillParams p) {
-    constexpr int NW = 4, DW = 256;
-    constexpr int RPW = 16 * RG, RWG = NW * RPW;       // rows per wave, per workgroup
-    using Dk = Decode<KV, NW, 256>;
-    constexpr int HB = (KV == KV_FP16) ? 16384 : 8192;   // bytes of one half-chunk (K then V)
-    // DMA vector memory operations of one half-chunk (INT8 scales not counted:
-    // waiting for one more operation than needed is only conservative)
-    constexpr int kHalfOps = (KV == KV_FP16) ? 16 : 8;
-    __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][2][HB];       // [buffer][half]
-    __shared__ __attribute__((aligned(16))) f32x4 s_scl[2][KV == KV_INT8 ? 64 : 1];
-    const int rg = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4, i = lane & 15;
-    const int Hq = p.num_q_heads, Hkv = p.kv.num_kv_heads, G = Hq / Hkv;
-    const int L = max(0, min(p.context_lens[b], p.max_context_len));
-    const int64_t qa = p.cu_q_lens[b];
-    const int n = min(max(p.cu_q_lens[b + 1] - p.cu_q_lens[b], 0), min(p.max_q_len, L));
-    const int nrows = n * G;
-    if (RWG * rg >= nrows) return;                                 // uniform: no rows here
-    const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
-    // this lane's rows: r = RWG rg + RPW wave + 16 j + i is query token r / G,
-    // head r % G, at position L - n + r / G, seeing keys below that plus one
-    bool live[RG];
-    int64_t row[RG];
-    int lim[RG];
-#pragma unroll
-    for (int j = 0; j < RG; ++j) {
-        const int r = RWG * rg + RPW * wave + 16 * j + i;
-        live[j] = r < nrows;
-        row[j] = (qa + (live[j] ? r : 0) / G) * Hq + (int64_t)kvh * G + (live[j] ? r : 0) % G;
-        lim[j] = live[j] ? L - n + r / G + 1 : 0;
-    }
-    // keys the workgroup's last row sees: the chunk range of every wave
-    const int kend = L - n + (min(RWG * rg + RWG - 1, nrows - 1)) / G + 1;
-    const int nch = (kend + 31) / 32;
-    int lim1[RG];
-#pragma unroll
-    for (int j = 0; j < RG; ++j) lim1[j] = min(lim[j], kend);
-
-    f16x8 qop[RG][2][4];
-#pragma unroll
-    for (int j = 0; j < RG; ++j) {
-        const f16* q = static_cast<const f16*>(p.q) + row[j] * DW;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-                qop[j][h][kc] = live[j] ? *reinterpret_cast<const f16x8*>(q + 128 * h + 64 * (kc >> 1) + 16 * g +
-                                                                          8 * (kc & 1))
-                                        : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-    float cscale = p.qk_scale_log2;
-    if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
-    float vscale = 1.0f;
-    if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
-    if constexpr (KV == KV_INT8) vscale = 1.0f / kInt8PFold;
-
-    WaveState2 st[RG];
-#pragma unroll
-    for (int j = 0; j < RG; ++j) {
-        st[j].m = -__builtin_inff();
-        st[j].l = 0.0f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) st[j].acc[h][c] = f32x4{0, 0, 0, 0};
-    }
-
-    int dsrc[Dk::kDmaPerPage], kofs[4], vofs[4];
-#pragma unroll
-    for (int q = 0; q < Dk::kDmaPerPage; ++q) dsrc[q] = Dk::dma_src(lane, q);
-    if constexpr (KV == KV_FP16) {
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) kofs[kc] = i * (2 * D) + 16 * ((8 * (kc >> 1) + 2 * g + (kc & 1)) ^ i);
-        // V token row t of page e/4 (t = 4g + e%4), chunk i (d = 8i..8i+7): slot i ^ t
-#pragma unroll
-        for (int x = 0; x < 4; ++x) vofs[x] = (4 * g + x) * (2 * D) + 16 * (i ^ (4 * g + x));
-    } else {
-        const int sk = Dk::swap02(i);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) kofs[h] = sk * D + 16 * ((4 * (h & 1) + g) ^ Dk::kap(sk));
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int sv = Dk::swap02(4 * g + x);
-            vofs[x] = sv * D + 16 * ((i >> 1) ^ Dk::kap(sv)) + 8 * (i & 1);
-        }
-    }
-    // chunk c's pages (blocks 2c, 2c+1) and validity bits; uniform
-    auto pages = [&](int c, int& pb0, int& pb1, bool& has1) __attribute__((always_inline)) {
-        const int nblk = (kend + BS - 1) / BS;
-        pb0 = bt[2 * c];
-        has1 = 2 * c + 1 < nblk;
-        pb1 = has1 ? bt[2 * c + 1] : -1;
-    };
-    // waves 0 and 1 move half `wave` of chunk c into buffer c % 2
-    auto issue = [&](int c, int& valid) __attribute__((always_inline)) {
-        int pb0, pb1;
-        bool has1;
-        pages(c, pb0, pb1, has1);
-        if (wave < 2)
-            pf256_issue<KV>(&s_kv[c & 1][wave][0], &s_scl[c & 1][0], p, kvh, pb0, pb1, has1, lane, dsrc,
-                            128 * Dk::EB * wave, wave == 0, valid);
-        else
-            valid = Dk::valid_bits(pb0, pb1, has1, p.kv.num_blocks);
-    };
-    int valid_cur = 0, valid_next = 0;
-    if (nch > 0) issue(0, valid_cur);
-    for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) {
-            issue(c + 1, valid_next);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kHalfOps) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        __syncthreads();                              // chunk c is in LDS for every wave
-        Chunk<KV> ch[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            typename Dk::Meta m;
-            m.valid_blk = valid_cur;
-            const uint8_t* lb = &s_kv[c & 1][h][0];
-            if constexpr (KV == KV_FP16) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    m.v16[e] = *reinterpret_cast<const u32x4*>(lb + 8192 + 4096 * (e >> 2) + vofs[e & 3]);
-            }
-            Dk::read(ch[h], m, lb, &s_scl[c & 1][0], kofs, vofs, g);
-        }
-        process_chunk_d256_rg<KV, RG>(st, ch, qop, cscale, 32 * c, kend, lim1, g);
-        __syncthreads();                              // every wave is done with buffer c % 2
-        valid_cur = valid_next;
-    }
-
-    // normalize and write this wave's rows: lane (i, g) holds row i's
-    // d = 128h + 32g + 8r + c in acc[h][c][r]
-#pragma unroll
-    for (int j = 0; j < RG; ++j) {
-        float l_run = st[j].l;
-        l_run += shfl_xor(l_run, 16);
-        l_run += shfl_xor(l_run, 32);
-        if (live[j]) {
-            const bool empty = !(l_run > 0.0f);
-            const float inv = empty ? 0.0f : vscale / l_run;
-            float* o = p.out + row[j] * DW;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    float* dst = o + 128 * h + 32 * g + 8 * rr;
-                    *reinterpret_cast<f32x4*>(dst) = f32x4{st[j].acc[h][0][rr], st[j].acc[h][1][rr],
-                                                           st[j].acc[h][2][rr], st[j].acc[h][3][rr]} * inv;
-                    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{st[j].acc[h][4][rr], st[j].acc[h][5][rr],
-                                                               st[j].acc[h][6][rr], st[j].acc[h][7][rr]} * inv;
-                }
-            if (g == 0) p.lse[row[j]] = empty ? -__builtin_inff() : (st[j].m + __builtin_log2f(l_run)) * kLn2;
-        }
-    }
-}
-
 }  // namespace
-
-hipError_t launch_prefill256(const PrefillParams& p, hipStream_t s) {
-    constexpr int RG = 2;                               // 16-row groups per wave: 128 rows per workgroup
-    const int G = p.num_q_heads / p.kv.num_kv_heads;
-    dim3 grid((unsigned)((p.max_q_len * G + 64 * RG - 1) / (64 * RG)), p.kv.num_kv_heads, p.num_seqs);
-    switch (p.kv.dtype) {
-    case KV_FP16: hipLaunchKernelGGL((paged_prefill256_kernel<KV_FP16, RG>), grid, dim3(256), 0, s, p); break;
-    case KV_E4M3: hipLaunchKernelGGL((paged_prefill256_kernel<KV_E4M3, RG>), grid, dim3(256), 0, s, p); break;
-    case KV_INT8: hipLaunchKernelGGL((paged_prefill256_kernel<KV_INT8, RG>), grid, dim3(256), 0, s, p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
 
 hipError_t launch_decode_partials(const DecodeParams& p0, hipStream_t s) {
     // The XCD-local placement only when every workgroup is resident at once
