@@ -607,10 +607,12 @@ template <int KV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill256_dma_kernel(PrefillParams p) {
     static_assert(KV != KV_FP16, "8-bit codes");
-    constexpr int ND = (KV == KV_INT8) ? 5 : 4;      // DMA instructions per subtile per wave
+    // DMA instructions per subtile per wave: codes (4), INT8 scales (1), page ids (1)
+    constexpr int ND = (KV == KV_INT8) ? 6 : 5;
     __shared__ __attribute__((aligned(1024))) uint8_t s_k[NBS][CB];
     __shared__ __attribute__((aligned(1024))) uint8_t s_v[NBS][CB];
     __shared__ __attribute__((aligned(16))) float s_sc[NBS][64];   // INT8: K scales by key, then V scales
+    __shared__ __attribute__((aligned(16))) int s_pid[8][64];       // page ids of subtile y at [y & 7][0..1]
 
     const int rb = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -711,14 +713,23 @@ void prefill256_dma_kernel(PrefillParams p) {
     const __attribute__((address_space(4))) int32_t* btc =
         (const __attribute__((address_space(4))) int32_t*)(uintptr_t)bt;
     auto page = [&](int idx) __attribute__((always_inline)) { return btc[min(idx, plast)]; };
+    // The key loop takes its page ids from LDS, where a DMA of every subtile
+    // step puts those of a subtile 2 NBS - 1 ahead (lane l: page 2y + (l & 1)):
+    // a scalar load in flight would make every LDS wait a wait for it.
+    auto issue_ids = [&](int y) __attribute__((always_inline)) {
+        dma4(bt + min(2 * y + (lane & 1), plast), lds_addr(&s_pid[y & 7][0]));
+    };
 
-    // ---- prologue: subtiles 0 .. NBS-2 in flight, 0 and 1 complete
-    int pg0 = 0, pg1 = 0;
+    // ---- prologue: the page ids that subtile 0 reads, then the DMA groups
+    // the loop would have issued before subtile 0 (codes of subtiles
+    // 0 .. NBS-2, page ids of NBS .. 2NBS-2); codes 0 and 1 and the first two
+    // groups' page ids complete
+    issue_ids(NBS - 1);
 #pragma unroll
-    for (int x = 0; x < NBS - 1; ++x) issue(x, page(2 * x), page(2 * x + 1));
-    int bnext = NBS - 1;                             // buffer of the next DMA'd subtile
-    pg0 = page(2 * (NBS - 1));                       // pages of that subtile
-    pg1 = page(2 * (NBS - 1) + 1);
+    for (int x = 0; x < NBS - 1; ++x) {
+        issue(x, page(2 * x), page(2 * x + 1));
+        issue_ids(NBS + x);
+    }
     wait_vm<(NBS - 3) * ND>();
     __syncthreads();
 
@@ -777,6 +788,8 @@ void prefill256_dma_kernel(PrefillParams p) {
         bool grow = false;
         f16x8 pp[2], kop[2];
         f32x4 sks[4], svs[4];
+        // page ids of subtile j + NBS - 1, whose codes part B sends for
+        const int2 ids = *reinterpret_cast<const int2*>(&s_pid[(j + NBS - 1) & 7][0]);
         // ---------------- part A
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -869,7 +882,9 @@ void prefill256_dma_kernel(PrefillParams p) {
         // subtile j + NBS - 1 into the buffer of subtile j - 1, before any
         // new LDS read (the page ids are scalar loads: a wait for them is a
         // wait for every LDS read in flight)
-        issue((bcur == 0) ? NBS - 1 : bcur - 1, pg0, pg1);
+        issue((bcur == 0) ? NBS - 1 : bcur - 1, __builtin_amdgcn_readfirstlane(ids.x),
+              __builtin_amdgcn_readfirstlane(ids.y));
+        issue_ids(j + 2 * NBS - 1);
         step_fence();
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -883,11 +898,6 @@ void prefill256_dma_kernel(PrefillParams p) {
             }
             if (i + PFV < 16) vraw[i % PFV] = vread(vbc, (i + PFV) >> 1, (i + PFV) & 1);
             acc[i >> 1] = mfma32(vop, pp[i & 1], acc[i >> 1]);
-            if (i == 3) {
-                // pages of the subtile after it (scalar loads, first used after the next barrier)
-                pg0 = page(2 * (j + NBS));
-                pg1 = page(2 * (j + NBS) + 1);
-            }
             if (i >= 16 - PFK) kraw[i - (16 - PFK)] = kread(sk0 + bnn * CB, i - (16 - PFK));   // subtile j + 2
             step_fence();
         }
