@@ -221,7 +221,7 @@ def test_d256_prefill_from_empty(plc, dtype):
 @pytest.mark.parametrize("chunk", [1, 2, 11, 16, 17, 64, 65])
 @pytest.mark.parametrize("prefix", [0, 1, 31, 32, 33, 2049])
 def test_d256_prefill_short_chunks_after_prefix(plc, chunk, prefix):
-    # row groups of 64 = 10 2/3 positions at six heads: groups cut positions
+    # wave tiles of 32 rows = 5 1/3 positions at six heads: tiles cut positions
     w = synthetic.generate(cases.spec([prefix + chunk], [chunk], hq=6, hkv=1, d=256, seed=671 + chunk))
     o, l = run_prefill(plc, w, "e4m3")
     ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, "e4m3"), SM)
