@@ -215,7 +215,16 @@ def _flatten(x, prefix="", out=None):
     return out
 
 
+def _profiled():
+    """Under rocprofv3 a child process inherits the profiler's preload, which
+    initialises the GPU before the smi tools' launchers re-exec themselves;
+    the clock and power readings are skipped there."""
+    return any(k.startswith("ROCPROF") for k in os.environ)
+
+
 def _smi(args, timeout=20):
+    if _profiled():
+        return None, "skipped under a profiler"
     try:
         r = subprocess.run(["amd-smi"] + args + ["--json"], capture_output=True, text=True,
                            timeout=timeout)
@@ -255,6 +264,8 @@ def smi_static():
                     (".clock." in kl and ("frequency_levels" in kl) and (".sys." in kl or ".mem." in kl)):
                 out[k] = v
     try:
+        if _profiled():
+            raise RuntimeError("skipped under a profiler")
         r = subprocess.run(["rocm-smi", "--showmaxpower", "--json"], capture_output=True, text=True,
                            timeout=20)
         j = json.loads(r.stdout)
@@ -270,6 +281,8 @@ def smi_under_load(replay, readings=3, max_s=8.0, warm_s=0.3):
     busy for warm_s before the first reading, so the clocks have ramped).
     Returns the first reading's fields plus, per clock/power field, the list
     of all readings."""
+    if _profiled():
+        return {"error": "skipped under a profiler"}
     n = 0
 
     def spin(until, p=None):
