@@ -808,7 +808,7 @@ def bench_decode_config(plc, synthetic, specs, name, dtypes, cpu, w=None):
 
 def bench_verify(plc, synthetic, specs, widths=(4, 16)):
     """Verification decode at the decode batch's shape (8 x 32768, E4M3,
-    partitions of 2048), 8 rotated cache copies, for a few draft widths."""
+    automatic partitions), 8 rotated cache copies, for a few draft widths."""
     import dataclasses
     res = {}
     for n in widths:
@@ -825,7 +825,7 @@ def bench_verify(plc, synthetic, specs, widths=(4, 16)):
         q = to_dev(w.q)
         T = int(w.cu_q_lens[-1])
         maxc = int(w.context_lens.max())
-        P = s.partition_tokens
+        P = 0                                   # the library's own partition choice
         ws = torch.zeros(plc.verify_workspace_size(s.num_seqs, T, s.num_q_heads, s.num_kv_heads,
                                                    s.head_dim, n, maxc, P),
                          dtype=torch.uint8, device="cuda")

@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libplc.so")
-SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill256.hip", "merge_append.hip"]
+SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill256.hip", "prefill_dma.hip", "merge_append.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -234,6 +234,48 @@ void mq_partitions(int32_t groups, int32_t num_kv_heads, int32_t max_q_len, int3
     if (*nparts < 1) *nparts = 1;
 }
 
+// Calls with a few query tokens per sequence whose rows of one (sequence, KV
+// head) (drafted positions x heads) exceed a few 16-row groups run as the
+// 128-row tiles of the 8-bit prefill kernel over key partitions, merged
+// afterwards: a tile shares each converted K and V subtile among 128 rows
+// where a decode workgroup shares it among 16 or 32.  E4M3 and INT8 caches
+// without a window (FP16 caches and windows keep the decode kernel).  The
+// row counts above which tiles win, measured over 8 x 32K contexts (E4M3):
+// head dim 128 (G = 8): 64 rows 28.9 us by the decode kernel against 34.3 by
+// tiles, 80 rows 42.8 against 35.3, 128 rows 43.8 against 38.1; head dim 256
+// (G = 6): 24 rows 69 against 89, 48 rows 123 against 94, 96 rows 227
+// against 98.
+constexpr int32_t kTileRows = 128;
+
+bool tile_eligible(int32_t head_dim, int32_t window, int32_t max_q_len, int32_t group) {
+    return window == 0 && (int64_t)max_q_len * group > (head_dim == kHeadDimWide ? 32 : 64);
+}
+
+// Key partitions of the tile path: an explicit size rounded up to whole
+// 32-key subtiles, else the shortest multiple of 32 keys (at least 256) that
+// keeps the grid within about one workgroup per compute unit (measured at 16
+// drafts over 8 x 32K: 37.8 us with 1024-key partitions and one workgroup
+// per CU, 40.4 with 512 and two: two tiles on a CU share its SIMDs no faster
+// than one, and the partials double).
+void tile_partitions(int64_t tiles, int32_t max_context_len, int32_t partition_tokens, int32_t* P,
+                     int32_t* nparts) {
+    int64_t p;
+    if (partition_tokens > 0) {
+        p = ((int64_t)partition_tokens + 31) / 32 * 32;
+    } else {
+        const int64_t want = std::max<int64_t>(1, (256 + tiles - 1) / tiles);
+        p = std::max<int64_t>(256, ((max_context_len + want - 1) / want + 31) / 32 * 32);
+    }
+    *P = (int32_t)p;
+    *nparts = max_context_len > 0 ? (int32_t)((max_context_len + p - 1) / p) : 1;
+}
+
+// (sequence, KV head, 128-row tile) units of a tile-path call
+int64_t tile_units(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_q_len) {
+    const int64_t G = num_q_heads / num_kv_heads;
+    return (int64_t)num_seqs * num_kv_heads * ((max_q_len * G + kTileRows - 1) / kTileRows);
+}
+
 // Per-device address of `scratch`, looked up on the first call on each
 // device, with that device current.
 constexpr int kMaxDevices = 64;
@@ -330,6 +372,10 @@ int plc_attn_prefill_paged(const void* q, int32_t num_q_heads, const plc_kv_cach
     p.qk_scale_log2 = sm_scale * 1.4426950408889634f;
     p.out = out;
     p.lse = lse;
+    p.partition_tokens = 0;
+    p.nparts = 1;
+    p.o_parts = nullptr;
+    p.lse_parts = nullptr;
     if (kv->head_dim == kHeadDimWide)
         return hip_status(plc::launch_prefill256(p, static_cast<hipStream_t>(stream)), "prefill launch");
     return hip_status(plc::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
@@ -454,8 +500,16 @@ size_t plc_window_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32
     // partial outputs and LSEs per query row
     // workgroup columns per (sequence, KV head): the launcher's grid
     const int32_t rg = plc::groups_per_workgroup(head_dim, true, ncg, P);
-    return decode_partial_bytes(rows, (int64_t)num_seqs * num_kv_heads, (ncg + rg - 1) / rg, nparts, P,
-                                head_dim);
+    size_t need = decode_partial_bytes(rows, (int64_t)num_seqs * num_kv_heads, (ncg + rg - 1) / rg, nparts,
+                                       P, head_dim);
+    // the cache's dtype is not an argument: room for the tile path as well
+    if (tile_eligible(head_dim, window_tokens, max_q_len, num_q_heads / num_kv_heads)) {
+        int32_t Pt = 0, npt = 0;
+        tile_partitions(tile_units(num_seqs, num_q_heads, num_kv_heads, max_q_len), max_context_len,
+                        partition_tokens, &Pt, &npt);
+        need = std::max(need, partial_bytes(rows, npt, head_dim));
+    }
+    return need;
 }
 
 size_t plc_verify_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
@@ -493,18 +547,53 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
                     partition_tokens, kv->block_size);
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
         return fail(PLC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
+    const size_t rows = (size_t)total_q_tokens * num_q_heads;
+    if (kv->dtype != PLC_KV_FP16 &&
+        tile_eligible(kv->head_dim, window_tokens, max_q_len, num_q_heads / kv->num_kv_heads)) {
+        int32_t Pt = 0, npt = 0;
+        tile_partitions(tile_units(num_seqs, num_q_heads, kv->num_kv_heads, max_q_len), max_context_len,
+                        partition_tokens, &Pt, &npt);
+        const size_t need = partial_bytes(rows, npt, kv->head_dim);
+        if (!workspace || workspace_bytes < need)
+            return fail(PLC_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                        workspace_bytes, workspace, need);
+        if ((rc = check_aligned(workspace, "workspace")) || (rc = check_aligned(out, "out"))) return rc;
+        plc::PrefillParams t;
+        t.q = q;
+        t.kv = view(kv);
+        t.block_tables = block_tables;
+        t.max_blocks = max_blocks;
+        t.cu_q_lens = cu_q_lens;
+        t.context_lens = context_lens;
+        t.num_seqs = num_seqs;
+        t.num_q_heads = num_q_heads;
+        t.max_q_len = max_q_len;
+        t.max_context_len = max_context_len;
+        t.qk_scale_log2 = sm_scale * 1.4426950408889634f;
+        t.out = nullptr;
+        t.lse = nullptr;
+        t.partition_tokens = Pt;
+        t.nparts = npt;
+        char* base = static_cast<char*>(workspace);
+        t.o_parts = reinterpret_cast<float*>(base);
+        t.lse_parts = reinterpret_cast<float*>(base + align_up(rows * npt * kv->head_dim * sizeof(float)));
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        if ((rc = hip_status(plc::launch_prefill_dma(t, s), "verify tile launch"))) return rc;
+        return hip_status(plc::launch_lse_merge(t.o_parts, t.lse_parts, (int32_t)rows, npt, kv->head_dim, out,
+                                                lse, s),
+                          "verify merge launch");
+    }
     const int32_t ncg = verify_row_groups(num_q_heads, kv->num_kv_heads, max_q_len);
     int32_t P = 0, nparts = 0;
     mq_partitions(num_seqs * ncg, kv->num_kv_heads, max_q_len, max_context_len, window_tokens,
                   partition_tokens, &P, &nparts);
-    const size_t need = plc_window_workspace_size(num_seqs, total_q_tokens, num_q_heads,
-                                                  kv->num_kv_heads, kv->head_dim, max_q_len,
-                                                  max_context_len, window_tokens, P);
+    const int32_t rg = plc::groups_per_workgroup(kv->head_dim, true, ncg, P);
+    const size_t need = decode_partial_bytes(rows, (int64_t)num_seqs * kv->num_kv_heads, (ncg + rg - 1) / rg,
+                                             nparts, P, kv->head_dim);
     if (!workspace || workspace_bytes < need)
         return fail(PLC_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
                     workspace_bytes, workspace, need);
     if ((rc = check_aligned(workspace, "workspace")) || (rc = check_aligned(out, "out"))) return rc;
-    const size_t rows = (size_t)total_q_tokens * num_q_heads;
     plc::DecodeParams p;
     p.q = q;
     p.kv = view(kv);

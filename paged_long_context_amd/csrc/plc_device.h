@@ -187,4 +187,45 @@ __device__ __forceinline__ T load_nt(const T* p) {
 template <typename T>
 __device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
 
+// ------------------------------------------------------------------ prefill tiles
+
+// Which key MFMA row rho of S^T holds within a 64-key tile: the swap of bits 2
+// and 3 makes the eight keys a lane owns for one PV step consecutive.  K is
+// stored in LDS in MFMA row order (the map is its own inverse).
+__device__ __forceinline__ int key_of_row(int rho) {
+    return (rho & 0x33) | ((rho & 0x8) >> 1) | ((rho & 0x4) << 1);
+}
+
+// Maximum of x over lanes l and l ^ 32 (the two halves of a score row) with
+// the gfx950 cross-half swap: after it, the first operand holds lanes 0-31 of
+// x in both halves and the second lanes 32-63 in both.  The nops cover the
+// VALU-write-to-swap and swap-to-VALU-read hazards, which the compiler does
+// not see inside the asm.
+__device__ __forceinline__ float max_halves(float x) {
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
+// x *= s on an accumulator held in an AGPR, through one scratch VGPR (the
+// compiler would otherwise give the accumulators VGPR homes for the rare
+// rescale, which costs Q operands their VGPRs for the whole loop)
+__device__ __forceinline__ float scale_acc(float x, float s) {
+    float t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(t) : "v"(s));
+    return x;
+}
+
+// The compiler moves no instruction across a step fence: a key loop written
+// as steps of one MFMA and a slice of other work keeps that interleaving.
+__device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+__device__ __forceinline__ void subtile_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+
 }  // namespace plc

@@ -121,12 +121,24 @@ struct PrefillParams {
     float qk_scale_log2;
     float* out;                 // f32 [T][Hq][D]
     float* lse;                 // f32 [T][Hq]
+    // 0: one pass over every visible key into out and lse.  > 0 (a multiple
+    // of 32, tiles of 8-bit caches only): partition k of a sequence is keys
+    // [k P, (k+1) P); each writes normalized partials of its rows to
+    // o_parts [T*Hq][nparts][D] and natural-log LSEs to lse_parts
+    // [T*Hq][nparts] (0 and -inf where a row sees none of its keys), and a
+    // sequence's n query tokens are its last n positions even when n exceeds
+    // its length (the rows before position 0 see no key)
+    int32_t partition_tokens;
+    int32_t nparts;
+    float* o_parts;
+    float* lse_parts;
 };
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill256(const PrefillParams& p, hipStream_t s);   // head dim 256
-
-// zero `bytes` (a multiple of 16, 16-byte aligned) with a kernel
+// tiles of 128 query rows over 8-bit caches whose codes reach LDS by DMA
+// (head dim 128 or 256), with or without key partitions
+hipError_t launch_prefill_dma(const PrefillParams& p, hipStream_t s);
 
 hipError_t launch_debug_e4m3(const uint8_t* codes, uint16_t* out, int32_t n, hipStream_t s);
 

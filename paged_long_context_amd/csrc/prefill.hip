@@ -35,14 +35,6 @@ constexpr int VSTR = KT + 8;            // V^T row stride in LDS (halves)
 constexpr int KBUF = KT * KSTR;         // halves
 constexpr int VBUF = D * VSTR;          // halves
 
-// Which key MFMA row rho of S^T holds (within a 64-key tile): the swap of
-// bits 2 and 3 makes the eight keys a lane owns for one PV step consecutive.
-// K is stored in LDS in MFMA row order, so LDS row rho holds key
-// key_of_row(rho) (the map is its own inverse).
-__device__ __forceinline__ int key_of_row(int rho) {
-    return (rho & 0x33) | ((rho & 0x8) >> 1) | ((rho & 0x4) << 1);
-}
-
 // K rows are 256 bytes without padding; the 16-byte chunk c of row rho lives
 // at chunk slot h(c) ^ g(rho), h(c) = (c >> 1) | 8(c & 1),
 // g(rho) = (rho & 7) | 8((rho ^ rho >> 3) & 1).  Operand reads (lanes = 16

@@ -40,13 +40,6 @@ constexpr int VBUF = D * VSTR;          // 36 KiB
 constexpr int ROWS = 128;               // query rows per workgroup
 constexpr int PF = 4;                   // MFMA operands read from LDS this many MFMAs ahead
 
-// Which key MFMA row rho of S^T holds within a 64-key tile: the swap of bits 2
-// and 3 makes the eight keys a lane owns for one PV step consecutive.  K is
-// stored in LDS in MFMA row order (the map is its own inverse).
-__device__ __forceinline__ int key_of_row(int rho) {
-    return (rho & 0x33) | ((rho & 0x8) >> 1) | ((rho & 0x4) << 1);
-}
-
 // LDS bank map (64 banks of 4 bytes).  K rows are 528 bytes, 4 banks apart
 // modulo 256 bytes: an operand read (16 consecutive rows, one 16-byte chunk
 // per lane) covers the 64 banks once, and a staging write (one row, chunks
@@ -87,18 +80,6 @@ __device__ __forceinline__ int per_lane(int x) {
     return y;
 }
 
-// Maximum of x over lanes l and l ^ 32 (the two halves of a score row) with
-// the gfx950 cross-half swap: after it, the first operand holds lanes 0-31 of
-// x in both halves and the second lanes 32-63 in both.  The nops cover the
-// VALU-write-to-swap and swap-to-VALU-read hazards, which the compiler does
-// not see inside the asm.
-__device__ __forceinline__ float max_halves(float x) {
-    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-}
-
-// K piece (page j, half h): 8 dimensions of one key
 template <int KV>
 __device__ __forceinline__ void load_k_piece(Stage<KV>& st, const PrefillParams& p, const StageAddr& sa, int j,
                                              int h, int key, int kend, int pg) {
@@ -213,24 +194,6 @@ __device__ __forceinline__ void store_vscales(const Stage<KV>& st, float* lvs, i
     }
     *reinterpret_cast<f32x4*>(lvs + kv0) = a;
     *reinterpret_cast<f32x4*>(lvs + kv0 + 4) = b;
-}
-
-// x *= s on an accumulator held in an AGPR, through one scratch VGPR (the
-// compiler would otherwise give the accumulators VGPR homes for the rare
-// rescale, which costs Q operands their VGPRs for the whole loop)
-__device__ __forceinline__ float scale_acc(float x, float s) {
-    float t;
-    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                 : "+a"(x), "=&v"(t) : "v"(s));
-    return x;
-}
-
-__device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0); }
-
-__device__ __forceinline__ void subtile_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Schedule of the key loop, per 32-key subtile j of tile T = j / 2, written
@@ -539,406 +502,16 @@ void prefill256_kernel(PrefillParams p) {
     }
 }
 
-// ------------------------------------------------------- 8-bit codes by DMA
-// E4M3 and INT8 caches: the codes of each 32-key subtile reach LDS
-// unconverted, by DMA (16 bytes per lane, one contiguous kilobyte per
-// instruction, no registers involved), NBS subtiles ahead of use; each wave
-// converts the K and V operands it reads.  LDS traffic per subtile is then
-// the 16 KiB of codes written and 64 KiB of operand reads, half of what fp16
-// tiles cost, and the staging needs no VALU work.  V^T operands come from V
-// stored as [key][d] through the gfx950 transposing read (ds_read_b64_tr_b8:
-// within each 16 lanes, lane 8p + i receives byte i of the eight rows that
-// lanes p, p + 2, ..., p + 14 address).  FP16 caches keep the register-staged
-// kernel above: their codes are twice as wide.
-
-constexpr int NBS = 6;                  // 32-key code buffers in flight
-constexpr int CB = 32 * D;              // bytes of one buffer's K (or V) codes
-constexpr int PFK = 3;                  // K code pairs read this many pairs ahead
-constexpr int PFV = 5;                  // V operands read this many MFMAs ahead
-
-// all zeros: the DMA source of pages whose id is outside the pool
-__device__ __attribute__((aligned(16))) uint8_t g_zero_page[BS * D];
-
-// chunk slot swizzles: chunk c (16 codes) of K row rho sits at slot c ^ (rho &
-// 15); chunk c of V row (key) k at slot c ^ vsig(k).  A K operand read (16
-// consecutive rows, one chunk) and a V transposing read (eight rows x two
-// adjacent chunks per 32 lanes) then touch distinct slots.
-__device__ __forceinline__ int vsig(int k) { return ((k & 7) << 1) | ((k >> 3) & 1); }
-
-// global_load_lds_dwordx4 with a 64-bit SGPR base and a 32-bit lane offset:
-// lane l's 16 bytes at base + off land at LDS dst + 16 l (dst wave-uniform).
-// Written as asm so that the compiler does not make every later LDS read
-// wait for it; the key loop waits with explicit vmcnt counts.  M0 (the LDS
-// base read at issue) is saved and restored.
-__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t dst) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(dst), "v"(off), "s"(base) : "memory");
-}
-
-// 4 bytes per lane from a 64-bit lane address to LDS dst + 4 l
-__device__ __forceinline__ void dma4(const void* src, uint32_t dst) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(dst), "v"(src) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-
-// Schedule per 32-key subtile j (buffer j % NBS), 16 steps per part:
-//   part A: S(j+1) = K Q^T, K code pairs read PFK pairs ahead and converted
-//           one step before their MFMAs, the online softmax of S(j) between;
-//           the last steps read the first V operands of part B;
-//   (rare rescale branch; wait for this wave's DMAs of subtile j+2; barrier)
-//   part B: O += V^T P(j)^T, V operands read PFV MFMAs ahead, converted one
-//           step before use; the DMAs of subtile j + NBS - 1 into the buffer
-//           of subtile j - 1, whose last reader was part B of j - 1; the
-//           last steps read the first K pairs of subtile j + 2.
-// Subtile x is first read at the end of part B of x - 2, after the barrier
-// of x - 2, by which every wave has waited for its own DMAs of x.
-template <int KV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefill256_dma_kernel(PrefillParams p) {
-    static_assert(KV != KV_FP16, "8-bit codes");
-    // DMA instructions per subtile per wave: codes (4), INT8 scales (1), page ids (1)
-    constexpr int ND = (KV == KV_INT8) ? 6 : 5;
-    __shared__ __attribute__((aligned(1024))) uint8_t s_k[NBS][CB];
-    __shared__ __attribute__((aligned(1024))) uint8_t s_v[NBS][CB];
-    __shared__ __attribute__((aligned(16))) float s_sc[NBS][64];   // INT8: K scales by key, then V scales
-    __shared__ __attribute__((aligned(16))) int s_pid[8][64];       // page ids of subtile y at [y & 7][0..1]
-
-    const int rb = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int Hq = p.num_q_heads, Hkv = p.kv.num_kv_heads, G = Hq / Hkv;
-    const int qa = p.cu_q_lens[b];
-    // lengths beyond the host-stated bounds are clamped so that no page id
-    // outside the table is ever read
-    const int L = max(0, min(p.context_lens[b], p.max_context_len));
-    const int n = min(max(p.cu_q_lens[b + 1] - qa, 0), min(p.max_q_len, L));
-    const int nrows = n * G;
-    const int r0 = ROWS * rb;
-    if (r0 >= nrows) return;
-    const int base = L - n;                          // position of the chunk's first token
-    const int rlast = min(r0 + ROWS, nrows) - 1;
-    const int kend = base + rlast / G + 1;           // keys [0, kend) are visible to someone
-    const int kfull = base + r0 / G + 1;             // keys [0, kfull) are visible to every row
-    const int nsub = (kend + 31) / 32;
-    const int nfull = min(kfull / 32, nsub);         // subtiles needing no mask
-    const int plast = (kend - 1) / BS;               // last page with a visible key
-    const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
-
-    const int h32 = lane >> 5, r32 = lane & 31;
-    int rowpos;
-    int64_t rowid;
-    bool rowok;
-    {
-        const int r = r0 + 32 * wave + r32;
-        rowok = r < nrows;
-        const int rc = rowok ? r : rlast;
-        rowpos = base + rc / G;
-        rowid = (int64_t)(qa + rc / G) * Hq + kvh * G + rc % G;
-    }
-    // Q operands.  MFMA kc of a subtile takes half (kc & 1) of K code pair
-    // kc >> 1, whose lane (row, h32) holds d = 32(kc>>1) + 16 h32 + [0,16), so
-    // lane (row, h32) of qop[kc] holds d = 32(kc>>1) + 16 h32 + 8(kc&1) + [0,8).
-    f16x8 qop[16];
-    {
-        const f16* q = static_cast<const f16*>(p.q) + rowid * D + 16 * h32;
-#pragma unroll
-        for (int kc = 0; kc < 16; ++kc) qop[kc] = *reinterpret_cast<const f16x8*>(q + 32 * (kc >> 1) + 8 * (kc & 1));
-    }
-    float cscale = p.qk_scale_log2;
-    if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
-    float vscale = 1.0f;
-    if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
-    if constexpr (KV == KV_INT8) vscale = 1.0f / kInt8PFold;
-    float m_ref = -__builtin_inff(), l_run = 0.0f;
-    const float grow_raw = (KV == KV_INT8) ? 0.0f : 8.0f / cscale;
-    f32x16 acc[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
-
-    // ---- DMA roles.  Wave w moves LDS rows 4w + (l >> 4) (page 2x of subtile
-    // x) and 16 + 4w + (l >> 4) (page 2x + 1) of each buffer's K and V, slot
-    // l & 15: K row rho holds key key_of_row(rho), V row k holds key k.
-    uint32_t kof[2], vof[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int row = 16 * h + 4 * wave + (lane >> 4), slot = lane & 15;
-        const int kk = key_of_row(row) & 15;
-        kof[h] = (uint32_t)(kk * D + 16 * (slot ^ (row & 15)));
-        vof[h] = (uint32_t)((row & 15) * D + 16 * (slot ^ vsig(row)));
-    }
-    const int64_t head_off = (int64_t)kvh * BS * D;
-    // the zero page's address, loaded once and kept in scalar registers
-    uint64_t zp = reinterpret_cast<uint64_t>(&g_zero_page[0]);
-    asm volatile("" : "+s"(zp));
-    // page base of (pg, kvh), or the zero page for an id outside the pool;
-    // selected with masks (uniform arithmetic, no branch)
-    auto page_base = [&](const void* cache, int pg) __attribute__((always_inline)) -> const uint8_t* {
-        const uint64_t m = 0ull - (uint64_t)((uint32_t)pg < (uint32_t)p.kv.num_blocks);
-        const uint64_t a = reinterpret_cast<uint64_t>(cache) + (uint64_t)((int64_t)pg * Hkv * BS * D + head_off);
-        return reinterpret_cast<const uint8_t*>((a & m) | (zp & ~m));
-    };
-    // INT8 scales of subtile x: lane l < 32 reads key l's K scale, lane 32 + l
-    // key l's V scale (every wave the same, which keeps the DMA counts equal)
-    auto scale_src = [&](int pg, int keyin) __attribute__((always_inline)) -> const float* {
-        const float* arr = (lane < 32) ? p.kv.k_scale : p.kv.v_scale;
-        const bool ok = (uint32_t)pg < (uint32_t)p.kv.num_blocks;
-        return ok ? arr + ((int64_t)pg * Hkv + kvh) * BS + keyin : reinterpret_cast<const float*>(zp) + keyin;
-    };
-    auto issue = [&](int bi, int pg0, int pg1) __attribute__((always_inline)) {
-        const uint32_t lk = lds_addr(&s_k[bi][0]) + 1024 * wave, lv = lds_addr(&s_v[bi][0]) + 1024 * wave;
-        dma16s(page_base(p.kv.k, pg0), kof[0], lk);
-        dma16s(page_base(p.kv.k, pg1), kof[1], lk + 4096);
-        dma16s(page_base(p.kv.v, pg0), vof[0], lv);
-        dma16s(page_base(p.kv.v, pg1), vof[1], lv + 4096);
-        if constexpr (KV == KV_INT8) {
-            const int key = lane & 31;
-            dma4(scale_src((key >> 4) ? pg1 : pg0, key & 15), lds_addr(&s_sc[bi][0]));
-        }
-    };
-    // page ids through the constant address space: scalar loads (the table is
-    // not written during the call), whose waits come right after a barrier
-    const __attribute__((address_space(4))) int32_t* btc =
-        (const __attribute__((address_space(4))) int32_t*)(uintptr_t)bt;
-    auto page = [&](int idx) __attribute__((always_inline)) { return btc[min(idx, plast)]; };
-    // The key loop takes its page ids from LDS, where a DMA of every subtile
-    // step puts those of a subtile 2 NBS - 1 ahead (lane l: page 2y + (l & 1)):
-    // a scalar load in flight would make every LDS wait a wait for it.
-    auto issue_ids = [&](int y) __attribute__((always_inline)) {
-        dma4(bt + min(2 * y + (lane & 1), plast), lds_addr(&s_pid[y & 7][0]));
-    };
-
-    // ---- prologue: the page ids that subtile 0 reads, then the DMA groups
-    // the loop would have issued before subtile 0 (codes of subtiles
-    // 0 .. NBS-2, page ids of NBS .. 2NBS-2); codes 0 and 1 and the first two
-    // groups' page ids complete
-    issue_ids(NBS - 1);
-#pragma unroll
-    for (int x = 0; x < NBS - 1; ++x) {
-        issue(x, page(2 * x), page(2 * x + 1));
-        issue_ids(NBS + x);
-    }
-    wait_vm<(NBS - 3) * ND>();
-    __syncthreads();
-
-    // ---- operand reads.  K code pair q of buffer bi: lane (r32, h32) reads
-    // 16 codes of row r32, chunk 2q + h32, at (kb + ka) ^ 32q; V operand
-    // (dt, hf): the transposing read at (vb + va + 4096 hf) ^ 32dt.
-    const uint32_t ka = (uint32_t)(r32 * D + 16 * (h32 ^ (r32 & 15)));
-    uint32_t va;
-    {
-        const int key = 8 * h32 + ((lane & 15) >> 1), gp = (lane >> 4) & 1;
-        va = (uint32_t)(key * D + 16 * (gp ^ vsig(key)) + 8 * (lane & 1));
-    }
-    const uint32_t sk0 = lds_addr(&s_k[0][0]), sv0 = lds_addr(&s_v[0][0]);
-    auto kread = [&](uint32_t kb, int q) __attribute__((always_inline)) {
-        return *(__attribute__((address_space(3))) const u32x4*)(uintptr_t)((kb + ka) ^ (32u * q));
-    };
-    auto vread = [&](uint32_t vb, int dt, int hf) __attribute__((always_inline)) {
-        typedef int v2i __attribute__((ext_vector_type(2)));
-        const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(uintptr_t)(((vb + va) ^ (32u * dt)) + 4096u * hf));
-        return u32x2{(uint32_t)r[0], (uint32_t)r[1]};
-    };
-
-    // ---- S of subtile 0
-    f32x16 sc;
-    {
-        u32x4 raw[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) raw[q] = kread(sk0, q);
-#pragma unroll
-        for (int kc = 0; kc < 16; ++kc) {
-            const u32x4& w = raw[kc >> 1];
-            const f16x8 kop = (kc & 1) ? codes8_to_f16x8<KV>(w[2], w[3]) : codes8_to_f16x8<KV>(w[0], w[1]);
-            sc = mfma32(kop, qop[kc], kc ? sc : f32x16{});
-        }
-    }
-    u32x4 kraw[PFK];                                 // K code pairs in flight (subtile j + 1)
-    u32x2 vraw[PFV];                                 // V operands in flight (subtile j)
-    {
-        const uint32_t kb1 = sk0 + CB;
-#pragma unroll
-        for (int q = 0; q < PFK; ++q) kraw[q] = kread(kb1, q);
-    }
-    int bcur = 0;                                    // buffer of subtile j
-
-    // one subtile j (buffer bcur)
-    auto sub = [&](auto mtag, int j) __attribute__((always_inline)) {
-        constexpr bool MASKED = decltype(mtag)::value;
-        constexpr int SO = (KV == KV_INT8) ? 2 : 0;  // INT8: two steps for the scale reads
-        const int bn = (bcur + 1 == NBS) ? 0 : bcur + 1, bnn = (bn + 1 == NBS) ? 0 : bn + 1;
-        const uint32_t kbn = sk0 + bn * CB;          // K codes of subtile j + 1
-        const uint32_t vbc = sv0 + bcur * CB;        // V codes of subtile j
-        const int k0 = 32 * j;
-        f32x16 sn;
-        float mloc = -__builtin_inff(), mx = 0.0f, m_new = 0.0f, moff = 0.0f, psum = 0.0f;
-        bool grow = false;
-        f16x8 pp[2], kop[2];
-        f32x4 sks[4], svs[4];
-        // page ids of subtile j + NBS - 1, whose codes part B sends for
-        const int2 ids = *reinterpret_cast<const int2*>(&s_pid[(j + NBS - 1) & 7][0]);
-        // ---------------- part A
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if ((i & 1) == 0) {
-                // pair i/2 arrived PFK pairs ago: both its operands, then the read PFK pairs ahead
-                const u32x4 w = kraw[(i >> 1) % PFK];
-                kop[0] = codes8_to_f16x8<KV>(w[0], w[1]);
-                kop[1] = codes8_to_f16x8<KV>(w[2], w[3]);
-                if ((i >> 1) + PFK < 8) kraw[(i >> 1) % PFK] = kread(kbn, (i >> 1) + PFK);
-            }
-            sn = mfma32(kop[i & 1], qop[i], i ? sn : f32x16{});
-            if (i >= 16 - PFV) vraw[i - (16 - PFV)] = vread(vbc, (i - (16 - PFV)) >> 1, (i - (16 - PFV)) & 1);
-            if constexpr (KV == KV_INT8)
-                if (i == 0) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int ko = 16 * (u >> 1) + 8 * h32 + 4 * (u & 1);
-                        sks[u] = *reinterpret_cast<const f32x4*>(&s_sc[bcur][ko]);
-                        svs[u] = *reinterpret_cast<const f32x4*>(&s_sc[bcur][32 + ko]);
-                    }
-                }
-            if (i >= SO && i < SO + 4) {
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    // element r of this lane's scores is key k0 + 16(r>>3) + 8 h32 + (r&7)
-                    const int r = 4 * (i - SO) + rr;
-                    float v = sc[r];
-                    if constexpr (KV == KV_INT8) v *= sks[r >> 2][r & 3];
-                    if constexpr (MASKED) {
-                        const int key = k0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
-                        v = (key <= rowpos) ? v : -__builtin_inff();
-                    }
-                    sc[r] = v;
-                    mloc = fmaxf(mloc, v);
-                }
-            }
-            if (i == SO + 4) {
-                mx = max_halves(mloc);
-                grow = mx > m_ref + grow_raw;
-                m_new = grow ? mx : m_ref;
-                moff = (m_new == -__builtin_inff()) ? 0.0f : -m_new * cscale;
-            }
-            if (i >= SO + 5 && i < SO + 13) {
-#pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const int r = 2 * (i - SO - 5) + rr;
-                    float pe = fast_exp2(__builtin_fmaf(sc[r], cscale, moff));
-                    psum += pe;
-                    if constexpr (KV == KV_INT8) {
-                        float vsr = svs[r >> 2][r & 3];
-                        if constexpr (MASKED) vsr = (k0 + 16 * (r >> 3) + 8 * h32 + (r & 7) < kend) ? vsr : 0.0f;
-                        pe *= vsr * kInt8PFold;
-                    }
-                    pp[r >> 3][r & 7] = (f16)pe;
-                }
-            }
-            step_fence();
-        }
-        pin(pp[0]);
-        pin(pp[1]);
-        pin(psum);
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
-            const float alpha = (m_ref == -__builtin_inff()) ? 0.0f : fast_exp2((m_ref - m_new) * cscale);
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[dt][r] = scale_acc(acc[dt][r], alpha);
-            asm volatile("s_nop 7" ::: "memory");
-        }
-        m_ref = m_new;
-        l_run += psum;
-        // this wave's DMAs of subtile j + 2 are complete; the barrier then
-        // publishes them and retires the buffer of subtile j - 1
-        wait_vm<(NBS - 4) * ND>();
-        subtile_barrier();
-        // ---------------- part B
-        // masked subtiles zero the V codes of keys past the visible end (the
-        // cache holds garbage there, and P = 0 times a NaN code is NaN)
-        uint32_t vm[2][2];
-        if constexpr (MASKED) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int cnt = min(max(kend - (k0 + 16 * hf + 8 * h32), 0), 8);
-                vm[hf][0] = cnt >= 4 ? 0xFFFFFFFFu : (1u << (8 * cnt)) - 1u;
-                vm[hf][1] = cnt >= 8 ? 0xFFFFFFFFu : (cnt <= 4 ? 0u : (1u << (8 * (cnt - 4))) - 1u);
-            }
-        }
-        f16x8 vop;
-        // subtile j + NBS - 1 into the buffer of subtile j - 1, before any
-        // new LDS read (the page ids are scalar loads: a wait for them is a
-        // wait for every LDS read in flight)
-        issue((bcur == 0) ? NBS - 1 : bcur - 1, __builtin_amdgcn_readfirstlane(ids.x),
-              __builtin_amdgcn_readfirstlane(ids.y));
-        issue_ids(j + 2 * NBS - 1);
-        step_fence();
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            {
-                u32x2 w = vraw[i % PFV];
-                if constexpr (MASKED) {
-                    w[0] &= vm[i & 1][0];
-                    w[1] &= vm[i & 1][1];
-                }
-                vop = codes8_to_f16x8<KV>(w[0], w[1]);
-            }
-            if (i + PFV < 16) vraw[i % PFV] = vread(vbc, (i + PFV) >> 1, (i + PFV) & 1);
-            acc[i >> 1] = mfma32(vop, pp[i & 1], acc[i >> 1]);
-            if (i >= 16 - PFK) kraw[i - (16 - PFK)] = kread(sk0 + bnn * CB, i - (16 - PFK));   // subtile j + 2
-            step_fence();
-        }
-        sc = sn;
-        bcur = bn;
-    };
-    using U = std::false_type;
-    using M = std::true_type;
-    for (int j = 0; j < nfull; ++j) sub(U{}, j);
-    for (int j = nfull; j < nsub; ++j) sub(M{}, j);
-    // DMAs still in flight write this workgroup's LDS: let them land first
-    wait_vm<0>();
-
-    // ---- epilogue: lanes l and l^32 hold halves of the same row's keys
-    const float l = l_run + shfl_xor(l_run, 32);
-    if (rowok) {
-        const float inv = vscale / l;
-        float* o = p.out + rowid * D;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int d = 32 * dt + 8 * a4 + 4 * h32;
-                *reinterpret_cast<f32x4*>(o + d) = f32x4{acc[dt][4 * a4 + 0], acc[dt][4 * a4 + 1],
-                                                         acc[dt][4 * a4 + 2], acc[dt][4 * a4 + 3]} * inv;
-            }
-        if (h32 == 0) p.lse[rowid] = (m_ref * cscale + __builtin_log2f(l)) * kLn2;
-    }
-}
-
 }  // namespace
 
 hipError_t launch_prefill256(const PrefillParams& p, hipStream_t s) {
+    if (p.kv.dtype != KV_FP16) return launch_prefill_dma(p, s);   // 8-bit codes by DMA
     const int G = p.num_q_heads / p.kv.num_kv_heads;
     dim3 grid((unsigned)(((int64_t)p.max_q_len * G + ROWS - 1) / ROWS), p.kv.num_kv_heads, p.num_seqs);
     if (grid.x == 0) return hipSuccess;
     const dim3 block(256);
     switch (p.kv.dtype) {
     case KV_FP16: hipLaunchKernelGGL(prefill256_kernel<KV_FP16>, grid, block, 0, s, p); break;
-    case KV_E4M3: hipLaunchKernelGGL(prefill256_dma_kernel<KV_E4M3>, grid, block, 0, s, p); break;
-    case KV_INT8: hipLaunchKernelGGL(prefill256_dma_kernel<KV_INT8>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

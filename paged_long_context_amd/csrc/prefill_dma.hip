@@ -1,0 +1,539 @@
+// Attention tiles of 128 query rows over 8-bit KV caches (E4M3, INT8) whose
+// codes reach LDS by DMA, at head dim 128 and 256, for gfx950: the chunked
+// causal prefill at head dim 256, and key partitions of the same tiles for
+// calls with up to 16 query tokens per sequence whose rows fill a tile.
+//
+// A workgroup is 4 waves = 128 query rows of one (sequence, KV head),
+// position-major (row r = query token r / G, head r % G, so the G heads of a
+// KV head share every K/V tile: 1Cat-vLLM README, Layer 2 "GQA Multi-Head
+// Packing"), one 32-row MFMA tile per wave.  Q operands and the O^T
+// accumulators stay in registers for the whole key loop.  S^T = K Q^T sums
+// over the whole head in one 32x32 accumulator (the pages split a 256-wide
+// head into halves on their hardware, Layer 2 "D256 Split-D"); O^T = V^T P^T
+// keeps one 32-dimension accumulator tile per 32 dimensions; QK and PV
+// accumulate in fp32 ("Performance First").  Keys are walked in subtiles of
+// 32 (two 16-token pages); subtiles wholly below the tile's first position
+// skip the causal mask (Layer 2 "Prefix / Causal-Tail Separation").
+//
+// The codes of each subtile reach LDS unconverted, by DMA (16 bytes per lane,
+// one contiguous kilobyte per instruction, no registers involved), NBS
+// subtiles ahead of use; each wave converts the K and V operands it reads
+// (the pages keep the same goals with register prefetch on V100: Layer 1 and
+// "Software-Reconstructed Async").  V^T operands come from V stored as
+// [key][d] through the gfx950 transposing read (ds_read_b64_tr_b8: within
+// each 16 lanes, lane 8p + i receives byte i of the eight rows that lanes p,
+// p + 2, ..., p + 14 address).
+//
+// Key partitions (Layer 2 "Split-KV3": partial states in fp32, merged after):
+// with partition_tokens > 0 the grid holds one workgroup per (row tile,
+// partition), each walking only its partition's subtiles and writing its
+// rows' normalized partial output and natural-log LSE; a row that sees no key
+// of the partition writes 0 and -inf.
+#include <type_traits>
+
+#include "plc_device.h"
+#include "plc_internal.h"
+
+namespace plc {
+namespace {
+
+constexpr int BS = 16;
+constexpr int ROWS = 128;               // query rows per workgroup
+constexpr int NBS = 6;                  // 32-key code buffers in flight
+constexpr int PFK = 3;                  // K code pairs read this many pairs ahead
+constexpr int PFV = 5;                  // V operands read this many MFMAs ahead
+
+// all zeros: the DMA source of pages whose id is outside the pool (one
+// (page, head) slice at the widest head)
+__device__ __attribute__((aligned(16))) uint8_t g_zero_page[BS * 256];
+
+// Shapes of the key loop per head dim.
+template <int DH>
+struct Geo {
+    static_assert(DH == 128 || DH == 256, "head dim");
+    static constexpr int NQ = DH / 16;      // K MFMAs per subtile = PV MFMAs = steps per part
+    static constexpr int NDT = DH / 32;     // O^T accumulator tiles
+    static constexpr int NKP = DH / 32;     // 32-code K pairs per row
+    static constexpr int NCH = DH / 16;     // 16-byte chunks per row
+    static constexpr int CB = 32 * DH;      // bytes of one subtile's K (or V) codes
+    static constexpr int NDK = DH / 128;    // K (and V) DMAs per wave per subtile
+    static constexpr int RPD = 1024 / DH;   // rows one DMA moves
+    static constexpr int NM = DH == 256 ? 4 : 2;   // part A steps of the row maximum
+    static constexpr int NE = DH == 256 ? 8 : 4;   // part A steps of the exponentials
+    // chunk slot swizzles.  Chunk c (16 codes) of K row rho sits at slot
+    // c ^ kswz(rho), chunk c of V row (key) k at slot c ^ vswz(k).  A K operand
+    // read (16 consecutive rows, one chunk) and a V transposing read (eight
+    // rows x two adjacent chunks per 32 lanes) then touch distinct banks:
+    // 256-byte rows all start on bank 0, so 16 distinct slots cover the 64
+    // banks; 128-byte rows alternate between banks 0 and 32, so the slot of
+    // rows of one parity must differ.
+    __device__ static int kswz(int rho) { return DH == 256 ? (rho & 15) : ((rho >> 1) & 7); }
+    __device__ static int vswz(int k) {
+        return DH == 256 ? (((k & 7) << 1) | ((k >> 3) & 1)) : (((k >> 1) & 3) << 1);
+    }
+};
+
+// global_load_lds_dwordx4 with a 64-bit SGPR base and a 32-bit lane offset:
+// lane l's 16 bytes at base + off land at LDS dst + 16 l (dst wave-uniform).
+// Written as asm so that the compiler does not make every later LDS read
+// wait for it; the key loop waits with explicit vmcnt counts.  M0 (the LDS
+// base read at issue) is saved and restored.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t dst) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(dst), "v"(off), "s"(base) : "memory");
+}
+
+// 4 bytes per lane from a 64-bit lane address to LDS dst + 4 l
+__device__ __forceinline__ void dma4(const void* src, uint32_t dst) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(dst), "v"(src) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// Schedule per 32-key subtile j (buffer j % NBS), NQ steps per part (one
+// MFMA each; the compiler moves nothing across steps):
+//   part A: S(j+1) = K Q^T, K code pairs read PFK pairs ahead and converted
+//           one step before their MFMAs, the online softmax of S(j) between;
+//           the last steps read the first V operands of part B;
+//   (rare rescale branch; wait for this wave's DMAs of subtile j+2; barrier)
+//   part B: O += V^T P(j)^T, V operands read PFV MFMAs ahead, converted one
+//           step before use; the DMAs of subtile j + NBS - 1 into the buffer
+//           of subtile j - 1, whose last reader was part B of j - 1; the
+//           last steps read the first K pairs of subtile j + 2.
+// Subtile x is first read at the end of part B of x - 2, after the barrier
+// of x - 2, by which every wave has waited for its own DMAs of x.  Subtiles
+// are counted from the first of the workgroup's key range.
+template <int KV, int DH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DH == 256 ? 1 : 2, DH == 256 ? 1 : 2)))
+void prefill_dma_kernel(PrefillParams p) {
+    static_assert(KV != KV_FP16, "8-bit codes");
+    using Gm = Geo<DH>;
+    constexpr int NQ = Gm::NQ, NDT = Gm::NDT, NKP = Gm::NKP, NCH = Gm::NCH, CB = Gm::CB;
+    constexpr int NDK = Gm::NDK, RPD = Gm::RPD, NM = Gm::NM, NE = Gm::NE;
+    // DMA instructions per subtile per wave: codes (2 NDK), INT8 scales (1), page ids (1)
+    constexpr int ND = 2 * NDK + 1 + (KV == KV_INT8 ? 1 : 0);
+    // part A: INT8 scale reads, row maximum, its exchange, exponentials
+    constexpr int SO = (KV == KV_INT8) ? (DH == 256 ? 2 : 1) : 0;
+    static_assert(SO + NM + 1 + NE <= NQ && PFV <= NQ && PFK <= NKP, "part A schedule");
+    // K codes of the NBS buffers, then their V codes; the epilogue reuses it
+    __shared__ __attribute__((aligned(1024))) uint8_t s_kv[2][NBS][CB];
+    __shared__ __attribute__((aligned(16))) float s_sc[NBS][64];   // INT8: K scales by key, then V scales
+    __shared__ __attribute__((aligned(16))) int s_pid[8][64];       // page ids of subtile y at [y & 7][0..1]
+
+    const bool split = p.partition_tokens > 0;
+    const int np = split ? p.nparts : 1;
+    const int rb = blockIdx.x / np, part = blockIdx.x - rb * np;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int Hq = p.num_q_heads, Hkv = p.kv.num_kv_heads, G = Hq / Hkv;
+    // The page ids of the first NBS - 1 subtiles of the workgroup's range,
+    // read before its lengths are known so that the two loads overlap: the
+    // range starts at subtile part * P / 32, and ids are clamped to the table
+    // row (ids past the context are never used; an id outside the pool is
+    // never dereferenced)
+    const int jb0 = split ? part * (p.partition_tokens / 32) : 0;
+    const int32_t* const bt = p.block_tables + (int64_t)b * p.max_blocks + 2 * jb0;
+    const __attribute__((address_space(4))) int32_t* const btc =
+        (const __attribute__((address_space(4))) int32_t*)(uintptr_t)bt;
+    int pid0[2 * (NBS - 1)];
+    {
+        const int pcap = max(p.max_blocks - 1 - 2 * jb0, 0);
+#pragma unroll
+        for (int x = 0; x < 2 * (NBS - 1); ++x) pid0[x] = btc[min(x, pcap)];
+    }
+    const int qa = p.cu_q_lens[b];
+    // lengths beyond the host-stated bounds are clamped so that no page id
+    // outside the table is ever read
+    const int L = max(0, min(p.context_lens[b], p.max_context_len));
+    // a prefill chunk holds at most L tokens; query tokens of a partitioned
+    // call are the last n positions even when n > L (the rows before position
+    // 0 see no key)
+    const int nq = min(max(p.cu_q_lens[b + 1] - qa, 0), p.max_q_len);
+    const int n = split ? nq : min(nq, L);
+    const int nrows = n * G;
+    const int r0 = ROWS * rb;
+    if (r0 >= nrows) return;
+    const int base = L - n;                          // position of the chunk's first token
+    const int rlast = min(r0 + ROWS, nrows) - 1;
+    const int kend = base + rlast / G + 1;           // keys [0, kend) are visible to someone
+    const int kfull = base + r0 / G + 1;             // keys [0, kfull) are visible to every row
+    const int nsub = max(kend, 0) / 32 + ((max(kend, 0) & 31) ? 1 : 0);
+    const int nfull = min(max(kfull, 0) / 32, nsub); // subtiles needing no mask
+
+    const int h32 = lane >> 5, r32 = lane & 31;
+    int rowpos;
+    int64_t rowid;
+    bool rowok;
+    {
+        const int r = r0 + 32 * wave + r32;
+        rowok = r < nrows;
+        const int rc = rowok ? r : rlast;
+        rowpos = base + rc / G;
+        rowid = (int64_t)(qa + rc / G) * Hq + kvh * G + rc % G;
+    }
+    float* const orow = split ? p.o_parts + (rowid * np + part) * DH : p.out + rowid * DH;
+    float* const lrow = split ? p.lse_parts + rowid * np + part : p.lse + rowid;
+
+    // this workgroup's subtiles [jb, je)
+    const int jb = jb0;
+    const int je = split ? min(nsub, jb + p.partition_tokens / 32) : nsub;
+    if (jb >= je) {                                  // no key of the partition is visible
+        if (rowok) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4)
+                    *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * a4 + 4 * h32) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (h32 == 0) *lrow = -__builtin_inff();
+        }
+        return;
+    }
+    const int nloc = je - jb;
+    const int nfloc = min(max(nfull - jb, 0), nloc);
+    // the range's page ids are counted from its first page; the loop's ids
+    // clamp to the range's last page (prefetches past the range reread it)
+    const int plast = min((kend - 1) / BS, 2 * je - 1) - 2 * jb;
+
+    // Q operands.  MFMA kc of a subtile takes half (kc & 1) of K code pair
+    // kc >> 1, whose lane (row, h32) holds d = 32(kc>>1) + 16 h32 + [0,16), so
+    // lane (row, h32) of qop[kc] holds d = 32(kc>>1) + 16 h32 + 8(kc&1) + [0,8).
+    f16x8 qop[NQ];
+    {
+        const f16* q = static_cast<const f16*>(p.q) + rowid * DH + 16 * h32;
+#pragma unroll
+        for (int kc = 0; kc < NQ; ++kc) qop[kc] = *reinterpret_cast<const f16x8*>(q + 32 * (kc >> 1) + 8 * (kc & 1));
+    }
+    float cscale = p.qk_scale_log2;
+    if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
+    float vscale = 1.0f;
+    if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
+    if constexpr (KV == KV_INT8) vscale = 1.0f / kInt8PFold;
+    float m_ref = -__builtin_inff(), l_run = 0.0f;
+    const float grow_raw = (KV == KV_INT8) ? 0.0f : 8.0f / cscale;
+    f32x16 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
+
+    // ---- DMA roles.  DMA h of wave w moves LDS rows 16 h + RPD w + l / NCH
+    // of each buffer's K and V, slot l % NCH, from page (16 h + RPD w) / 16 of
+    // the subtile: K row rho holds key key_of_row(rho), V row k holds key k.
+    uint32_t kof[NDK], vof[NDK];
+#pragma unroll
+    for (int h = 0; h < NDK; ++h) {
+        const int row = 16 * h + RPD * wave + lane / NCH, slot = lane % NCH;
+        const int kk = key_of_row(row) & 15;
+        kof[h] = (uint32_t)(kk * DH + 16 * (slot ^ Gm::kswz(row)));
+        vof[h] = (uint32_t)((row & 15) * DH + 16 * (slot ^ Gm::vswz(row)));
+    }
+    const int64_t head_off = (int64_t)kvh * BS * DH;
+    // the zero page's address, loaded once and kept in scalar registers
+    uint64_t zp = reinterpret_cast<uint64_t>(&g_zero_page[0]);
+    asm volatile("" : "+s"(zp));
+    // page base of (pg, kvh), or the zero page for an id outside the pool;
+    // selected with masks (uniform arithmetic, no branch)
+    auto page_base = [&](const void* cache, int pg) __attribute__((always_inline)) -> const uint8_t* {
+        const uint64_t m = 0ull - (uint64_t)((uint32_t)pg < (uint32_t)p.kv.num_blocks);
+        const uint64_t a = reinterpret_cast<uint64_t>(cache) + (uint64_t)((int64_t)pg * Hkv * BS * DH + head_off);
+        return reinterpret_cast<const uint8_t*>((a & m) | (zp & ~m));
+    };
+    // INT8 scales of subtile x: lane l < 32 reads key l's K scale, lane 32 + l
+    // key l's V scale (every wave the same, which keeps the DMA counts equal)
+    auto scale_src = [&](int pg, int keyin) __attribute__((always_inline)) -> const float* {
+        const float* arr = (lane < 32) ? p.kv.k_scale : p.kv.v_scale;
+        const bool ok = (uint32_t)pg < (uint32_t)p.kv.num_blocks;
+        return ok ? arr + ((int64_t)pg * Hkv + kvh) * BS + keyin : reinterpret_cast<const float*>(zp) + keyin;
+    };
+    auto issue = [&](int bi, int pg0, int pg1) __attribute__((always_inline)) {
+        const uint32_t lk = lds_addr(&s_kv[0][bi][0]), lv = lds_addr(&s_kv[1][bi][0]);
+#pragma unroll
+        for (int h = 0; h < NDK; ++h) {
+            const int first = 16 * h + RPD * wave;   // wave-uniform
+            const int pg = (first >> 4) ? pg1 : pg0;
+            dma16s(page_base(p.kv.k, pg), kof[h], lk + first * DH);
+            dma16s(page_base(p.kv.v, pg), vof[h], lv + first * DH);
+        }
+        if constexpr (KV == KV_INT8) {
+            const int key = lane & 31;
+            dma4(scale_src((key >> 4) ? pg1 : pg0, key & 15), lds_addr(&s_sc[bi][0]));
+        }
+    };
+    // The key loop takes its page ids from LDS, where a DMA of every subtile
+    // step puts those of a subtile 2 NBS - 1 ahead (lane l: page 2y + (l & 1)):
+    // a scalar load in flight would make every LDS wait a wait for it.
+    auto issue_ids = [&](int y) __attribute__((always_inline)) {
+        dma4(bt + min(2 * y + (lane & 1), plast), lds_addr(&s_pid[y & 7][0]));
+    };
+
+    // ---- prologue: the page ids that subtile 0 reads, then the DMA groups
+    // the loop would have issued before subtile 0 (codes of subtiles
+    // 0 .. NBS-2, page ids of NBS .. 2NBS-2); codes 0 and 1 and the first two
+    // groups' page ids complete
+    issue_ids(NBS - 1);
+#pragma unroll
+    for (int x = 0; x < NBS - 1; ++x) {
+        issue(x, pid0[2 * x], pid0[2 * x + 1]);
+        issue_ids(NBS + x);
+    }
+    wait_vm<(NBS - 3) * ND>();
+    __syncthreads();
+
+    // ---- operand reads.  K code pair q of buffer bi: lane (r32, h32) reads
+    // 16 codes of row r32, chunk 2q + h32, at (kb + ka) ^ 32q; V operand
+    // (dt, hf): the transposing read at ((vb + va) ^ 32dt) + 16 DH hf.
+    const uint32_t ka = (uint32_t)(r32 * DH + 16 * (h32 ^ Gm::kswz(r32)));
+    uint32_t va;
+    {
+        const int key = 8 * h32 + ((lane & 15) >> 1), gp = (lane >> 4) & 1;
+        va = (uint32_t)(key * DH + 16 * (gp ^ Gm::vswz(key)) + 8 * (lane & 1));
+    }
+    const uint32_t sk0 = lds_addr(&s_kv[0][0][0]), sv0 = lds_addr(&s_kv[1][0][0]);
+    auto kread = [&](uint32_t kb, int q) __attribute__((always_inline)) {
+        return *(__attribute__((address_space(3))) const u32x4*)(uintptr_t)((kb + ka) ^ (32u * q));
+    };
+    auto vread = [&](uint32_t vb, int dt, int hf) __attribute__((always_inline)) {
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(uintptr_t)(((vb + va) ^ (32u * dt)) + 16u * DH * hf));
+        return u32x2{(uint32_t)r[0], (uint32_t)r[1]};
+    };
+
+    // ---- S of subtile 0
+    f32x16 sc;
+    {
+        u32x4 raw[NKP];
+#pragma unroll
+        for (int q = 0; q < NKP; ++q) raw[q] = kread(sk0, q);
+#pragma unroll
+        for (int kc = 0; kc < NQ; ++kc) {
+            const u32x4& w = raw[kc >> 1];
+            const f16x8 kop = (kc & 1) ? codes8_to_f16x8<KV>(w[2], w[3]) : codes8_to_f16x8<KV>(w[0], w[1]);
+            sc = mfma32(kop, qop[kc], kc ? sc : f32x16{});
+        }
+    }
+    u32x4 kraw[PFK];                                 // K code pairs in flight (subtile j + 1)
+    u32x2 vraw[PFV];                                 // V operands in flight (subtile j)
+    {
+        const uint32_t kb1 = sk0 + CB;
+#pragma unroll
+        for (int q = 0; q < PFK; ++q) kraw[q] = kread(kb1, q);
+    }
+    int bcur = 0;                                    // buffer of subtile j
+
+    // one subtile j of the range (buffer bcur)
+    auto sub = [&](auto mtag, int j) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
+        constexpr int RM = 16 / NM, RE = 16 / NE;    // scores per max step, per exp step
+        const int bn = (bcur + 1 == NBS) ? 0 : bcur + 1, bnn = (bn + 1 == NBS) ? 0 : bn + 1;
+        const uint32_t kbn = sk0 + bn * CB;          // K codes of subtile j + 1
+        const uint32_t vbc = sv0 + bcur * CB;        // V codes of subtile j
+        const int k0 = 32 * (jb + j);                // its first key
+        f32x16 sn;
+        float mloc = -__builtin_inff(), mx = 0.0f, m_new = 0.0f, moff = 0.0f, psum = 0.0f;
+        bool grow = false;
+        f16x8 pp[2], kop[2];
+        f32x4 sks[4], svs[4];
+        // page ids of subtile j + NBS - 1, whose codes part B sends for
+        const int2 ids = *reinterpret_cast<const int2*>(&s_pid[(j + NBS - 1) & 7][0]);
+        // ---------------- part A
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            if ((i & 1) == 0) {
+                // pair i/2 arrived PFK pairs ago: both its operands, then the read PFK pairs ahead
+                const u32x4 w = kraw[(i >> 1) % PFK];
+                kop[0] = codes8_to_f16x8<KV>(w[0], w[1]);
+                kop[1] = codes8_to_f16x8<KV>(w[2], w[3]);
+                if ((i >> 1) + PFK < NKP) kraw[(i >> 1) % PFK] = kread(kbn, (i >> 1) + PFK);
+            }
+            sn = mfma32(kop[i & 1], qop[i], i ? sn : f32x16{});
+            if (i >= NQ - PFV) vraw[i - (NQ - PFV)] = vread(vbc, (i - (NQ - PFV)) >> 1, (i - (NQ - PFV)) & 1);
+            if constexpr (KV == KV_INT8)
+                if (i == 0) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int ko = 16 * (u >> 1) + 8 * h32 + 4 * (u & 1);
+                        sks[u] = *reinterpret_cast<const f32x4*>(&s_sc[bcur][ko]);
+                        svs[u] = *reinterpret_cast<const f32x4*>(&s_sc[bcur][32 + ko]);
+                    }
+                }
+            if (i >= SO && i < SO + NM) {
+#pragma unroll
+                for (int rr = 0; rr < RM; ++rr) {
+                    // element r of this lane's scores is key k0 + 16(r>>3) + 8 h32 + (r&7)
+                    const int r = RM * (i - SO) + rr;
+                    float v = sc[r];
+                    if constexpr (KV == KV_INT8) v *= sks[r >> 2][r & 3];
+                    if constexpr (MASKED) {
+                        const int key = k0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
+                        v = (key <= rowpos) ? v : -__builtin_inff();
+                    }
+                    sc[r] = v;
+                    mloc = fmaxf(mloc, v);
+                }
+            }
+            if (i == SO + NM) {
+                mx = max_halves(mloc);
+                grow = mx > m_ref + grow_raw;
+                m_new = grow ? mx : m_ref;
+                moff = (m_new == -__builtin_inff()) ? 0.0f : -m_new * cscale;
+            }
+            if (i >= SO + NM + 1 && i < SO + NM + 1 + NE) {
+#pragma unroll
+                for (int rr = 0; rr < RE; ++rr) {
+                    const int r = RE * (i - SO - NM - 1) + rr;
+                    float pe = fast_exp2(__builtin_fmaf(sc[r], cscale, moff));
+                    psum += pe;
+                    if constexpr (KV == KV_INT8) {
+                        float vsr = svs[r >> 2][r & 3];
+                        if constexpr (MASKED) vsr = (k0 + 16 * (r >> 3) + 8 * h32 + (r & 7) < kend) ? vsr : 0.0f;
+                        pe *= vsr * kInt8PFold;
+                    }
+                    pp[r >> 3][r & 7] = (f16)pe;
+                }
+            }
+            step_fence();
+        }
+        pin(pp[0]);
+        pin(pp[1]);
+        pin(psum);
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+            const float alpha = (m_ref == -__builtin_inff()) ? 0.0f : fast_exp2((m_ref - m_new) * cscale);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[dt][r] = scale_acc(acc[dt][r], alpha);
+            asm volatile("s_nop 7" ::: "memory");
+        }
+        m_ref = m_new;
+        l_run += psum;
+        // this wave's DMAs of subtile j + 2 are complete; the barrier then
+        // publishes them and retires the buffer of subtile j - 1
+        wait_vm<(NBS - 4) * ND>();
+        subtile_barrier();
+        // ---------------- part B
+        // masked subtiles zero the V codes of keys past the visible end (the
+        // cache holds garbage there, and P = 0 times a NaN code is NaN)
+        uint32_t vm[2][2];
+        if constexpr (MASKED) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int cnt = min(max(kend - (k0 + 16 * hf + 8 * h32), 0), 8);
+                vm[hf][0] = cnt >= 4 ? 0xFFFFFFFFu : (1u << (8 * cnt)) - 1u;
+                vm[hf][1] = cnt >= 8 ? 0xFFFFFFFFu : (cnt <= 4 ? 0u : (1u << (8 * (cnt - 4))) - 1u);
+            }
+        }
+        f16x8 vop;
+        // subtile j + NBS - 1 into the buffer of subtile j - 1, before any
+        // new LDS read
+        issue((bcur == 0) ? NBS - 1 : bcur - 1, __builtin_amdgcn_readfirstlane(ids.x),
+              __builtin_amdgcn_readfirstlane(ids.y));
+        issue_ids(j + 2 * NBS - 1);
+        step_fence();
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            {
+                u32x2 w = vraw[i % PFV];
+                if constexpr (MASKED) {
+                    w[0] &= vm[i & 1][0];
+                    w[1] &= vm[i & 1][1];
+                }
+                vop = codes8_to_f16x8<KV>(w[0], w[1]);
+            }
+            if (i + PFV < NQ) vraw[i % PFV] = vread(vbc, (i + PFV) >> 1, (i + PFV) & 1);
+            acc[i >> 1] = mfma32(vop, pp[i & 1], acc[i >> 1]);
+            if (i >= NQ - PFK) kraw[i - (NQ - PFK)] = kread(sk0 + bnn * CB, i - (NQ - PFK));   // subtile j + 2
+            step_fence();
+        }
+        sc = sn;
+        bcur = bn;
+    };
+    using U = std::false_type;
+    using M = std::true_type;
+    for (int j = 0; j < nfloc; ++j) sub(U{}, j);
+    for (int j = nfloc; j < nloc; ++j) sub(M{}, j);
+    // DMAs still in flight write this workgroup's LDS: let them land first
+    wait_vm<0>();
+
+    // ---- epilogue: lanes l and l^32 hold halves of the same row's keys; a
+    // row with no visible key in the range (partitions only) writes 0, -inf
+    const float l = l_run + shfl_xor(l_run, 32);
+    const bool empty = !(l > 0.0f);
+    const float inv = empty ? 0.0f : vscale / l;
+    if (rowok && h32 == 0) *lrow = empty ? -__builtin_inff() : (m_ref * cscale + __builtin_log2f(l)) * kLn2;
+    // O leaves through LDS, 64 dimensions at a time: the MFMA layout gives each
+    // store instruction 32-byte pieces of 32 rows, the wave's LDS tile (rows
+    // of 64 floats + 4 of padding) four whole 256-byte row pieces.  Lane l
+    // stores rows 4i + l/16, floats 4(l%16) + [0,4); the row addresses come
+    // from the lanes that own the rows (null for rows past the tile).
+    __syncthreads();                                 // every wave is past its last LDS read
+    constexpr int TS = 68;                           // LDS tile row stride (floats)
+    float* const tile = reinterpret_cast<float*>(&s_kv[0][0][0]) + wave * 32 * TS;
+    const uint64_t mine = rowok ? reinterpret_cast<uint64_t>(orow) : 0ull;
+    float* dst[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int src = (4 * i + (lane >> 4)) << 2;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)mine);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(mine >> 32));
+        dst[i] = reinterpret_cast<float*>(((uint64_t)hi << 32) | lo);
+    }
+#pragma unroll
+    for (int ps = 0; ps < DH / 64; ++ps) {
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int dt = 2 * ps + dd;
+                *reinterpret_cast<f32x4*>(tile + r32 * TS + 32 * dd + 8 * a4 + 4 * h32) =
+                    f32x4{acc[dt][4 * a4 + 0], acc[dt][4 * a4 + 1], acc[dt][4 * a4 + 2], acc[dt][4 * a4 + 3]} * inv;
+            }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(tile + (4 * i + (lane >> 4)) * TS + 4 * (lane & 15));
+            if (dst[i]) *reinterpret_cast<f32x4*>(dst[i] + 64 * ps + 4 * (lane & 15)) = v;
+        }
+    }
+}
+
+template <int DH>
+hipError_t launch_dh(const PrefillParams& p, hipStream_t s) {
+    const int G = p.num_q_heads / p.kv.num_kv_heads;
+    const int64_t tiles = ((int64_t)p.max_q_len * G + ROWS - 1) / ROWS;
+    const int64_t np = p.partition_tokens > 0 ? p.nparts : 1;
+    const dim3 grid((unsigned)(tiles * np), p.kv.num_kv_heads, p.num_seqs);
+    if (grid.x == 0) return hipSuccess;
+    const dim3 block(256);
+    switch (p.kv.dtype) {
+    case KV_E4M3: hipLaunchKernelGGL((prefill_dma_kernel<KV_E4M3, DH>), grid, block, 0, s, p); break;
+    case KV_INT8: hipLaunchKernelGGL((prefill_dma_kernel<KV_INT8, DH>), grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_dma(const PrefillParams& p, hipStream_t s) {
+    if (p.partition_tokens < 0 || p.partition_tokens % 32 != 0 || (p.partition_tokens > 0 && p.nparts < 1))
+        return hipErrorInvalidValue;
+    switch (p.kv.head_dim) {
+    case 128: return launch_dh<128>(p, s);
+    case 256: return launch_dh<256>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace plc

@@ -270,3 +270,25 @@ def test_d256_prefill_full_size_subsample(plc):
     rows = synthetic.subsample_rows(8192, 12, 96, seed=0xD2, tile=32)
     ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, "e4m3"), SM, rows=rows)
     assert_close(o, l, ro, rl, rows=rows, what="d256 prefill 8192 after 122880")
+
+
+@pytest.mark.parametrize("dtype", ["e4m3", "int8"])
+def test_d256_verify_tiles_edges(plc, dtype):
+    # 16 drafts x 6 heads = 96 rows per KV head: the 128-row tiles over key
+    # partitions, then the merge.  The first sequence is given 7 keys on the
+    # device for its 16 query tokens (rows before position 0 see no key:
+    # out 0, lse -inf); one sequence has 6 query tokens, one none
+    ctx = [30, 600, 4100, 33, 77]
+    ql = [16, 16, 16, 6, 0]
+    w = synthetic.generate(cases.spec(ctx, ql, hq=12, hkv=2, d=256, seed=680))
+    cache, bt = device_cache(plc, w, dtype)
+    dctx = w.context_lens.copy()
+    dctx[0] = 7
+    w2 = synthetic.Workload(**{**w.__dict__, "context_lens": dctx})
+    ro, rl = cases.oracle_attention(w2, cases.oracle_cache(w2, dtype), SM)
+    for P in [0, 32, 1024]:
+        o, l = plc.attn_verify_paged(dev(w.q), cache, bt, dev(w.cu_q_lens), dev(dctx), 16, 4100, P, SM)
+        torch.cuda.synchronize()
+        o, l = host(o), host(l)
+        assert np.isneginf(l[:9]).all() and np.all(o[:9] == 0.0)
+        assert_close(o, l, ro, rl, what="d256 verify tiles %s P=%d" % (dtype, P))

@@ -128,3 +128,38 @@ def test_verify_full_decode_shape_sampled(plc):
     o, l = run_verify(plc, w, "e4m3", 2048)
     ro, rl = oracle_verify(w, "e4m3", rows=rows)
     assert_close(o, l, ro, rl, rows=rows, what="verify 8x32768 n=4")
+
+
+@pytest.mark.parametrize("dtype", ["e4m3", "int8"])
+def test_verify_tiles_edges(plc, dtype):
+    # 16 drafts x 8 heads = 128 rows per (sequence, KV head): the 128-row
+    # tiles over key partitions, then the merge.  The first sequence is given
+    # 10 keys on the device for its 16 query tokens (rows before position 0
+    # see no key: out 0, lse -inf); one sequence has 9 query tokens (a part-
+    # filled tile), one has none; partitions explicit (32, 48 -> 64 keys,
+    # 1024) and automatic
+    ctx = [40, 300, 64, 5000, 33, 777]
+    ql = [16, 16, 16, 16, 9, 0]
+    w = synthetic.generate(cases.spec(ctx, ql, hq=8, hkv=1, seed=417))
+    cache, bt = device_cache(plc, w, dtype)
+    dctx = w.context_lens.copy()
+    dctx[0] = 10
+    w2 = synthetic.Workload(**{**w.__dict__, "context_lens": dctx})
+    ro, rl = oracle_verify(w2, dtype)
+    for P in [0, 32, 48, 1024]:
+        o, l = plc.attn_verify_paged(dev(w.q), cache, bt, dev(w.cu_q_lens), dev(dctx), 16, 5000, P,
+                                     sm_scale())
+        torch.cuda.synchronize()
+        o, l = host(o), host(l)
+        assert np.isneginf(l[:6]).all() and np.all(o[:6] == 0.0)
+        assert_close(o, l, ro, rl, what="verify tiles %s P=%d" % (dtype, P))
+
+
+def test_verify_tiles_two_row_tiles_per_head(plc):
+    # G = 16: 16 drafts x 16 heads = 256 rows per KV head, two tiles each,
+    # two KV heads; mixed draft counts leave the second tile part-filled
+    w = synthetic.generate(cases.spec([3000, 129, 2100], [16, 12, 5], hq=32, hkv=2, seed=418))
+    for dtype in ["e4m3", "int8"]:
+        o, l = run_verify(plc, w, dtype, 0, max_q_len=16)
+        ro, rl = oracle_verify(w, dtype)
+        assert_close(o, l, ro, rl, what="verify G=16 tiles %s" % dtype)
