@@ -107,7 +107,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 //           the last steps read the first V operands of part B;
 //   (rare rescale branch; wait for this wave's DMAs of subtile j+2; barrier)
 //   part B: O += V^T P(j)^T, V operands read PFV MFMAs ahead, converted one
-//           step before use; the DMAs of subtile j + NBS - 1 into the buffer
+//           step before use, consecutive MFMAs on different accumulator
+//           tiles (operand o: tile o % NDT, key half o / NDT); the DMAs of subtile j + NBS - 1 into the buffer
 //           of subtile j - 1, whose last reader was part B of j - 1; the
 //           last steps read the first K pairs of subtile j + 2.
 // Subtile x is first read at the end of part B of x - 2, after the barrier
@@ -358,7 +359,7 @@ void prefill_dma_kernel(PrefillParams p) {
                 if ((i >> 1) + PFK < NKP) kraw[(i >> 1) % PFK] = kread(kbn, (i >> 1) + PFK);
             }
             sn = mfma32(kop[i & 1], qop[i], i ? sn : f32x16{});
-            if (i >= NQ - PFV) vraw[i - (NQ - PFV)] = vread(vbc, (i - (NQ - PFV)) >> 1, (i - (NQ - PFV)) & 1);
+            if (i >= NQ - PFV) vraw[i - (NQ - PFV)] = vread(vbc, (i - (NQ - PFV)) % NDT, (i - (NQ - PFV)) / NDT);
             if constexpr (KV == KV_INT8)
                 if (i == 0) {
 #pragma unroll
@@ -447,13 +448,13 @@ void prefill_dma_kernel(PrefillParams p) {
             {
                 u32x2 w = vraw[i % PFV];
                 if constexpr (MASKED) {
-                    w[0] &= vm[i & 1][0];
-                    w[1] &= vm[i & 1][1];
+                    w[0] &= vm[i / NDT][0];
+                    w[1] &= vm[i / NDT][1];
                 }
                 vop = codes8_to_f16x8<KV>(w[0], w[1]);
             }
-            if (i + PFV < NQ) vraw[i % PFV] = vread(vbc, (i + PFV) >> 1, (i + PFV) & 1);
-            acc[i >> 1] = mfma32(vop, pp[i & 1], acc[i >> 1]);
+            if (i + PFV < NQ) vraw[i % PFV] = vread(vbc, (i + PFV) % NDT, (i + PFV) / NDT);
+            acc[i % NDT] = mfma32(vop, pp[i / NDT], acc[i % NDT]);
             if (i >= NQ - PFK) kraw[i - (NQ - PFK)] = kread(sk0 + bnn * CB, i - (NQ - PFK));   // subtile j + 2
             step_fence();
         }
