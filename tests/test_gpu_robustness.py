@@ -84,6 +84,21 @@ def test_int8_prefill_with_fp16_extreme_values(plc, d, hq, hkv):
     print("int8 prefill d%d: max|do|/max|V| %.2e" % (d, e), flush=True)
 
 
+@pytest.mark.parametrize("d,hq,hkv,n", [(128, 8, 1, 4), (128, 8, 1, 16), (256, 12, 2, 16)])
+def test_int8_verify_with_fp16_extreme_values(plc, d, hq, hkv, n):
+    # 4 drafts x 8 heads keeps the decode kernel; 16 drafts run as prefill
+    # tiles over key partitions (both head dims)
+    w = synthetic.generate(cases.spec([3000, 2049, 40], [n, n, n], hq=hq, hkv=hkv, d=d, seed=821 + d + n))
+    vmax = big_values(w, 19)
+    cache, bt = device_cache(plc, w, "int8")
+    o, l = plc.attn_verify_paged(dev(w.q), cache, bt, dev(w.cu_q_lens), dev(w.context_lens), n, 3000, 0,
+                                 sm_scale(d))
+    torch.cuda.synchronize()
+    ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, "int8"), sm_scale(d))
+    e = assert_close_scaled(host(o), host(l), ro, rl, vmax, "int8 verify d%d n=%d extreme V" % (d, n))
+    print("int8 verify d%d n=%d: max|do|/max|V| %.2e" % (d, n, e), flush=True)
+
+
 @pytest.mark.parametrize("dtype", ["e4m3", "int8"])
 def test_workspace_reused_across_shapes(plc, dtype):
     """One workspace, never initialized (filled with NaN bytes here), serves
@@ -92,19 +107,26 @@ def test_workspace_reused_across_shapes(plc, dtype):
     wa = synthetic.generate(cases.spec([5000, 17, 2049], [1, 1, 1], hq=8, hkv=1, seed=821))
     wb = synthetic.generate(cases.spec([900, 4100, 33, 70, 16], [3, 4, 1, 2, 2], hq=16, hkv=4,
                                        seed=822))
+    # 16 drafts x 8 heads: verification as prefill tiles over key partitions
+    wc = synthetic.generate(cases.spec([3000, 700, 20], [16, 16, 9], hq=8, hkv=1, seed=823))
     ca, bta = device_cache(plc, wa, dtype)
     cb, btb = device_cache(plc, wb, dtype)
+    cc, btc = device_cache(plc, wc, dtype)
     ws = torch.full((1 << 26,), 0xFF, dtype=torch.uint8, device="cuda")
     ref_a = cases.oracle_attention(wa, cases.oracle_cache(wa, dtype), sm_scale())
     ref_b = cases.oracle_attention(wb, cases.oracle_cache(wb, dtype), sm_scale())
+    ref_c = cases.oracle_attention(wc, cases.oracle_cache(wc, dtype), sm_scale())
     for it, part in enumerate([512, 0, 48]):
         o, l = plc.attn_decode_paged(dev(wa.q), ca, bta, dev(wa.context_lens), 5000, part, sm_scale(),
                                      workspace=ws)
         ob, lb = plc.attn_verify_paged(dev(wb.q), cb, btb, dev(wb.cu_q_lens), dev(wb.context_lens), 4,
                                        4100, 16 * (it + 1), sm_scale(), workspace=ws)
+        oc, lc = plc.attn_verify_paged(dev(wc.q), cc, btc, dev(wc.cu_q_lens), dev(wc.context_lens), 16,
+                                       3000, part, sm_scale(), workspace=ws)
         torch.cuda.synchronize()
         assert_close(host(o), host(l), *ref_a, what="decode call %d" % it)
         assert_close(host(ob), host(lb), *ref_b, what="verify call %d" % it)
+        assert_close(host(oc), host(lc), *ref_c, what="verify tiles call %d" % it)
 
 
 def shard_tables(w, ranks, interleave):
