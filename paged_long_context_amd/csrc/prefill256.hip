@@ -22,6 +22,11 @@
 // "Software-Reconstructed Async" section give the same goals on V100).  Tiles
 // wholly below the workgroup's first position skip the causal mask (Layer 2
 // "Prefix / Causal-Tail Separation").
+//
+// The launcher takes this register-staged kernel for FP16 caches only; E4M3
+// and INT8 caches go to the tile kernel whose codes reach LDS by DMA
+// (prefill_dma.hip), measured faster for 8-bit codes.  The kernel stays
+// written for every dtype (its INT8 and E4M3 paths are not instantiated).
 #include <type_traits>
 
 #include "plc_device.h"
