@@ -108,9 +108,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 //   (rare rescale branch; wait for this wave's DMAs of subtile j+2; barrier)
 //   part B: O += V^T P(j)^T, V operands read PFV MFMAs ahead, converted one
 //           step before use, consecutive MFMAs on different accumulator
-//           tiles (operand o: tile o % NDT, key half o / NDT); the DMAs of subtile j + NBS - 1 into the buffer
-//           of subtile j - 1, whose last reader was part B of j - 1; the
-//           last steps read the first K pairs of subtile j + 2.
+//           tiles (operand o: tile o % NDT, key half o / NDT); the DMAs of
+//           subtile j + NBS - 1 into the buffer of subtile j - 1, whose last
+//           reader was part B of j - 1; the last steps read the first K pairs
+//           of subtile j + 2.
 // Subtile x is first read at the end of part B of x - 2, after the barrier
 // of x - 2, by which every wave has waited for its own DMAs of x.  Subtiles
 // are counted from the first of the workgroup's key range.
