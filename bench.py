@@ -806,14 +806,16 @@ def bench_decode_config(plc, synthetic, specs, name, dtypes, cpu, w=None):
     return out
 
 
-def bench_verify(plc, synthetic, specs, widths=(4, 16)):
+def bench_verify(plc, synthetic, specs, widths=(4, 16), spec_name="verify"):
     """Verification decode at the decode batch's shape (8 x 32768, E4M3,
-    automatic partitions), 8 rotated cache copies, for a few draft widths."""
+    automatic partitions), 8 rotated cache copies, for a few draft widths;
+    spec_name "d256" takes the head dim 256 batch (12 q / 2 kv) instead."""
     import dataclasses
     res = {}
     for n in widths:
-        sp = dataclasses.replace(specs["verify"], q_lens=[n] * len(specs["verify"].context_lens))
-        log("generating verify n=%d" % n)
+        sp = dataclasses.replace(specs[spec_name], q_lens=[n] * len(specs[spec_name].context_lens))
+        tag = "verify" if spec_name == "verify" else spec_name + " verify"
+        log("generating %s n=%d" % (tag, n))
         w = synthetic.generate(sp)
         s = w.spec
         caches, bt = build_cache(plc, w, "e4m3", 8)
@@ -850,11 +852,11 @@ def bench_verify(plc, synthetic, specs, widths=(4, 16)):
             "frac_of_hbm_peak": round(vb / ev / 1e9 / HBM_PEAK_GBS, 4),
             "tflops": round(fl / ev / 1e12, 2),
         }
-        log("verify n=%d: %.2f us = %.0f GB/s (%.1f%% of HBM), %.1f TFLOP/s"
-            % (n, ev * 1e6, vb / ev / 1e9, 100 * vb / ev / 1e9 / HBM_PEAK_GBS, fl / ev / 1e12))
+        log("%s n=%d: %.2f us = %.0f GB/s (%.1f%% of HBM), %.1f TFLOP/s"
+            % (tag, n, ev * 1e6, vb / ev / 1e9, 100 * vb / ev / 1e9 / HBM_PEAK_GBS, fl / ev / 1e12))
         del caches, ws, out, lse, q
         torch.cuda.empty_cache()
-    res["workload"] = specs["verify"].description + "; widths as listed"
+    res["workload"] = specs[spec_name].description + "; widths as listed"
     return res
 
 
@@ -1030,6 +1032,8 @@ def main():
                 res.update(bench_decode_config(plc, synthetic, specs, "c5", [name[3:]], cpu))
             elif name == "verify":
                 res["verify_e4m3"] = bench_verify(plc, synthetic, specs)
+            elif name == "verify_d256":
+                res["verify_d256_e4m3"] = bench_verify(plc, synthetic, specs, widths=(16,), spec_name="d256")
             elif name == "window":
                 res["draft_window_e4m3"] = bench_window(plc, synthetic, specs)
             elif name == "d256":
@@ -1061,6 +1065,7 @@ def main():
         extra.update(bench_decode_config(plc, synthetic, specs, "c4", ["e4m3"], cpu))
         extra.update(bench_decode_config(plc, synthetic, specs, "c5", ["fp16", "e4m3", "int8"], cpu))
         extra["verify_e4m3"] = bench_verify(plc, synthetic, specs)
+        extra["verify_d256_e4m3"] = bench_verify(plc, synthetic, specs, widths=(16,), spec_name="d256")
         extra["draft_window_e4m3"] = bench_window(plc, synthetic, specs)
         extra["d256_decode"] = bench_d256(plc, synthetic, specs)
         extra["d256_prefill"] = bench_d256_prefill(plc, synthetic, specs)
