@@ -279,8 +279,9 @@ def smi_under_load(replay, readings=3, max_s=8.0, warm_s=0.3):
     """GPU clocks and power read by amd-smi `readings` times while `replay`
     keeps the GPU busy (up to 16 replays queued between synchronizations, and
     busy for warm_s before the first reading, so the clocks have ramped).
-    Returns the first reading's fields plus, per clock/power field, the list
-    of all readings."""
+    Returns the fields of the reading with the highest socket power (a
+    reading can fall between two queued replays and show the idle clock)
+    plus, per clock/power field, the list of all readings."""
     if _profiled():
         return {"error": "skipped under a profiler"}
     n = 0
@@ -310,7 +311,12 @@ def smi_under_load(replay, readings=3, max_s=8.0, warm_s=0.3):
             p.kill()
             got.append({"error": "%s: %s" % (type(e).__name__, str(e)[:200])})
     torch.cuda.synchronize()
-    res = dict(got[0])
+
+    def power(g):
+        v = g.get("power.socket_power")
+        return v if isinstance(v, (int, float)) else -1
+
+    res = dict(max(got, key=power))
     keys = [k for k in res if k.startswith("clock.gfx_0") or k.startswith("clock.mem_0") or k.startswith("power")]
     res["readings"] = {k: [g.get(k) for g in got] for k in keys}
     return res

@@ -75,6 +75,87 @@ __global__ __launch_bounds__(64 * kMergeWavesPerBlock) void lse_merge_kernel(
     if (slice == 0 && lane == 0) lse_out[row] = empty ? -__builtin_inff() : M + __builtin_logf(wsum);
 }
 
+// Head dims 128 and 256: one wave per row.  Lane (h, c) = (l / 32, l % 32)
+// takes the parts of parity h and columns 4c + 128s + [0,4) (s < D / 128),
+// so one load instruction moves the pieces of two adjacent parts (contiguous
+// in o_parts) and a batch of 32 parts is 16 such loads per column block, all
+// in one round trip.  Lane k (mod 32) loads part k's LSE and computes its
+// weight against the batch maximum; readlane hands the weights of parts 2j
+// and 2j + 1 to every lane, which keeps its parity's.  The even and odd
+// parities are summed separately, each in index order, and added at the end.
+template <int D>
+__global__ __launch_bounds__(64) void lse_merge_rows_kernel(
+    const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int rows, int nparts,
+    float* __restrict__ out, float* __restrict__ lse_out) {
+    constexpr int NS = D / 128;
+    constexpr int KB = 32;                             // parts per batch
+    const int lane = threadIdx.x, h = lane >> 5, c = lane & 31;
+    const int row = blockIdx.x;
+    if (row >= rows) return;
+    const float NEG = -__builtin_inff();
+    const float* lp = lse_parts + (int64_t)row * nparts;
+    const float* op = o_parts + (int64_t)row * nparts * D + 4 * c;
+    float M = NEG, wsum = 0.0f;
+    f32x4 acc[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = 0; kb < nparts; kb += KB) {
+        const int kn = min(KB, nparts - kb);
+        // this lane's parts kb + 2j + h (a part past the batch reads part kb
+        // and gets weight 0)
+        f32x4 ov[KB / 2][NS];
+#pragma unroll
+        for (int j = 0; j < KB / 2; ++j) {
+            const int k = (2 * j + h < kn) ? kb + 2 * j + h : kb;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) ov[j][s] = *reinterpret_cast<const f32x4*>(op + (int64_t)k * D + 128 * s);
+        }
+        const float lk = c < kn ? lp[kb + c] : NEG;
+        // all of the batch's loads in one round trip
+#pragma unroll
+        for (int j = 0; j < KB / 2; ++j)
+#pragma unroll
+            for (int s = 0; s < NS; ++s) pin(ov[j][s]);
+        float mb = lk;
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) mb = fmaxf(mb, shfl_xor(mb, off));
+        mb = fmaxf(mb, M);
+        if (mb == NEG) continue;                       // nothing visible yet
+        const float sc = (M == NEG) ? 0.0f : fast_exp2((M - mb) * kLog2e);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[s] *= sc;
+        wsum *= sc;
+        const float wl = (lk == NEG) ? 0.0f : fast_exp2((lk - mb) * kLog2e);
+#pragma unroll
+        for (int j = 0; j < KB / 2; ++j)
+            if (2 * j < kn) {
+                const float w0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), 2 * j));
+                const float w1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), 2 * j + 1));
+                const float w = (2 * j + h < kn) ? (h ? w1 : w0) : 0.0f;
+                wsum += w;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) acc[s] += w * ov[j][s];
+            }
+        M = mb;
+    }
+    // the two parities' sums, even first (every lane takes part in each
+    // exchange: a permute reads nothing from lanes outside the exec mask)
+    const float wother = shfl_xor(wsum, 32);
+    const float wtot = h ? wother + wsum : wsum + wother;
+    const bool empty = !(wtot > 0.0f);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float other = shfl_xor(acc[s][e], 32);
+            o[e] = h ? other + acc[s][e] : acc[s][e] + other;
+        }
+        if (h == 0) *reinterpret_cast<f32x4*>(out + (int64_t)row * D + 128 * s + 4 * c) = empty ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : o / wtot;
+    }
+    if (lane == 0) lse_out[row] = empty ? NEG : M + __builtin_logf(wtot);
+}
+
 // ------------------------------------------------------------------ append
 //
 // D / 8 lanes (16 for head dim 128, 32 for 256) per (token, KV head, K-or-V)
@@ -147,6 +228,15 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_
                             int32_t nparts, int32_t head_dim, float* out, float* lse_out,
                             hipStream_t s) {
     if (rows == 0) return hipSuccess;
+    if (head_dim == 128 || head_dim == 256) {
+        if (head_dim == 128)
+            hipLaunchKernelGGL((lse_merge_rows_kernel<128>), dim3(rows), dim3(64), 0, s, o_parts, lse_parts, rows,
+                               nparts, out, lse_out);
+        else
+            hipLaunchKernelGGL((lse_merge_rows_kernel<256>), dim3(rows), dim3(64), 0, s, o_parts, lse_parts, rows,
+                               nparts, out, lse_out);
+        return hipGetLastError();
+    }
     const int64_t waves = (int64_t)rows * ((head_dim + 63) / 64);
     dim3 grid((unsigned)((waves + kMergeWavesPerBlock - 1) / kMergeWavesPerBlock));
     hipLaunchKernelGGL(lse_merge_kernel, grid, dim3(64 * kMergeWavesPerBlock), 0, s, o_parts, lse_parts, rows,
