@@ -228,7 +228,11 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_
                             int32_t nparts, int32_t head_dim, float* out, float* lse_out,
                             hipStream_t s) {
     if (rows == 0) return hipSuccess;
-    if (head_dim == 128 || head_dim == 256) {
+    // the one-wave-per-row kernel moves 16-byte pieces: taken when both
+    // value arrays are 16-byte aligned (every workspace and decode-family
+    // output is; plc_lse_merge callers may pass any float pointers)
+    const bool aligned = ((reinterpret_cast<uintptr_t>(o_parts) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+    if (aligned && (head_dim == 128 || head_dim == 256)) {
         if (head_dim == 128)
             hipLaunchKernelGGL((lse_merge_rows_kernel<128>), dim3(rows), dim3(64), 0, s, o_parts, lse_parts, rows,
                                nparts, out, lse_out);

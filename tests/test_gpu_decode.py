@@ -130,18 +130,37 @@ def test_decode_partials_then_merge_equals_decode(plc):
 
 
 def test_lse_merge_against_oracle(plc):
+    # head dims 128 and 256 take the one-wave-per-row kernel (parts in batches
+    # of 32, even and odd parts per lane half), other widths the generic one
     rng = np.random.default_rng(204)
-    for rows, nparts, d in [(5, 1, 128), (64, 16, 128), (7, 300, 128), (3, 5, 64), (2, 9, 256)]:
+    for rows, nparts, d in [(5, 1, 128), (64, 16, 128), (7, 300, 128), (3, 5, 64), (2, 9, 256),
+                            (4, 33, 128), (6, 31, 128), (3, 64, 256), (4, 2, 128), (5, 97, 256),
+                            (3, 40, 200)]:
         o = rng.standard_normal((rows, nparts, d)).astype(np.float32)
         l = (rng.standard_normal((rows, nparts)) * 30).astype(np.float32)
         l[rng.random((rows, nparts)) < 0.2] = -np.inf
         l[0, :] = -np.inf                      # an all-empty row
-        go, gl = plc.lse_merge(dev(o), dev(l))
+        if nparts > 32:
+            l[1, :32] = -np.inf                # a first batch with no visible part
+            l[1, -1] = 2.0
+            l[2, 32:64] = -np.inf              # an empty batch between visible ones
+            l[2, 0] = 1.0
+        if rows > 3:
+            l[3, :-1] = -np.inf                # only the last part visible
+            l[3, -1] = 5.0
         ro, rl = oracle.lse_merge(o, l)
-        go, gl = host(go), host(gl)
-        assert np.all(go[0] == 0) and gl[0] == -np.inf
-        assert np.abs(go[1:] - ro[1:]).max() <= 1e-5
-        assert (np.abs(gl[1:] - rl[1:]) / np.maximum(1, np.abs(rl[1:]))).max() <= 1e-6
+        # aligned arrays, then o_parts and out 4 bytes off a 16-byte boundary
+        # (views one float into larger buffers: the generic kernel takes them)
+        ob = torch.empty(o.size + 1, dtype=torch.float32, device="cuda")
+        ob[1:] = dev(o).reshape(-1)
+        outb = torch.empty(rows * d + 1, dtype=torch.float32, device="cuda")
+        for src, dst in [(dev(o), None), (ob[1:].view(rows, nparts, d), outb[1:].view(rows, d))]:
+            go, gl = plc.lse_merge(src, dev(l), out=dst)
+            go, gl = host(go), host(gl)
+            empty = np.isneginf(rl)            # row 0, and any row the random -inf emptied
+            assert empty[0] and np.array_equal(np.isneginf(gl), empty) and np.all(go[empty] == 0)
+            assert np.abs(go[~empty] - ro[~empty]).max() <= 1e-5
+            assert (np.abs(gl[~empty] - rl[~empty]) / np.maximum(1, np.abs(rl[~empty]))).max() <= 1e-6
 
 
 def test_decode_is_deterministic_and_placement_independent(plc):
