@@ -292,3 +292,15 @@ def test_d256_verify_tiles_edges(plc, dtype):
         o, l = host(o), host(l)
         assert np.isneginf(l[:9]).all() and np.all(o[:9] == 0.0)
         assert_close(o, l, ro, rl, what="d256 verify tiles %s P=%d" % (dtype, P))
+
+
+def test_d256_verify16_full_shape_sampled(plc):
+    # the bench's head dim 256 verification at full size: 8 x 32768 context,
+    # 12 q / 2 kv, 16 drafts (96 rows per KV head: tiles over key partitions),
+    # automatic partitions; a seeded sample of rows against the oracle
+    ctx = [32768] * 8
+    w = synthetic.generate(cases.spec(ctx, [16] * 8, hq=12, hkv=2, d=256, seed=681))
+    rows = np.sort(np.random.default_rng(681).choice(16 * 12 * 8, 40, replace=False))
+    o, l = run_mq(plc, w, "e4m3", 0, 0)
+    ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, "e4m3"), SM, rows=rows)
+    assert_close(o, l, ro, rl, rows=rows, what="d256 verify 8x32768 n=16")

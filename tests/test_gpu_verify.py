@@ -163,3 +163,15 @@ def test_verify_tiles_two_row_tiles_per_head(plc):
         o, l = run_verify(plc, w, dtype, 0, max_q_len=16)
         ro, rl = oracle_verify(w, dtype)
         assert_close(o, l, ro, rl, what="verify G=16 tiles %s" % dtype)
+
+
+def test_verify16_full_shape_sampled(plc):
+    # the bench's 16-draft call at full size: 8 x 32768 context, 8 q / 1 kv,
+    # automatic partitions (128-row tiles over 32 partitions of 1,024 keys);
+    # the oracle checks a seeded sample of rows spread over every sequence
+    ctx = [32768] * 8
+    w = synthetic.generate(cases.spec(ctx, [16] * 8, hq=8, hkv=1, seed=419))
+    rows = np.sort(np.random.default_rng(419).choice(128 * 8, 48, replace=False))
+    o, l = run_verify(plc, w, "e4m3", 0)
+    ro, rl = oracle_verify(w, "e4m3", rows=rows)
+    assert_close(o, l, ro, rl, rows=rows, what="verify 8x32768 n=16")
