@@ -222,7 +222,11 @@ void prefill_dma_kernel(PrefillParams p) {
     if constexpr (KV == KV_E4M3) vscale = p.kv.v_scale[kvh];
     if constexpr (KV == KV_INT8) vscale = 1.0f / kInt8PFold;
     float m_ref = -__builtin_inff(), l_run = 0.0f;
-    const float grow_raw = (KV == KV_INT8) ? 0.0f : 8.0f / cscale;
+    // lazy rescaling: the reference maximum moves only when a score passes
+    // it by 2^8 in probability.  INT8's P operand carries 64 sigma_v, so there
+    // the allowance shrinks per subtile to keep 2^allow * 64 * sigma_max below
+    // 64,000 (< 65,504, the largest finite fp16)
+    const float grow_raw = 8.0f / cscale, inv_cs = 1.0f / cscale;
     f32x16 acc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -343,7 +347,7 @@ void prefill_dma_kernel(PrefillParams p) {
         const uint32_t vbc = sv0 + bcur * CB;        // V codes of subtile j
         const int k0 = 32 * (jb + j);                // its first key
         f32x16 sn;
-        float mloc = -__builtin_inff(), mx = 0.0f, m_new = 0.0f, moff = 0.0f, psum = 0.0f;
+        float mloc = -__builtin_inff(), mx = 0.0f, m_new = 0.0f, moff = 0.0f, psum = 0.0f, smax = 0.0f;
         bool grow = false;
         f16x8 pp[2], kop[2];
         f32x4 sks[4], svs[4];
@@ -376,7 +380,12 @@ void prefill_dma_kernel(PrefillParams p) {
                     // element r of this lane's scores is key k0 + 16(r>>3) + 8 h32 + (r&7)
                     const int r = RM * (i - SO) + rr;
                     float v = sc[r];
-                    if constexpr (KV == KV_INT8) v *= sks[r >> 2][r & 3];
+                    if constexpr (KV == KV_INT8) {
+                        v *= sks[r >> 2][r & 3];
+                        float s = svs[r >> 2][r & 3];
+                        if constexpr (MASKED) s = (k0 + 16 * (r >> 3) + 8 * h32 + (r & 7) < kend) ? s : 0.0f;
+                        smax = fmaxf(smax, s);
+                    }
                     if constexpr (MASKED) {
                         const int key = k0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
                         v = (key <= rowpos) ? v : -__builtin_inff();
@@ -387,7 +396,10 @@ void prefill_dma_kernel(PrefillParams p) {
             }
             if (i == SO + NM) {
                 mx = max_halves(mloc);
-                grow = mx > m_ref + grow_raw;
+                float allow = grow_raw;
+                if constexpr (KV == KV_INT8)   // log2(1000 / sigma_max), at most 8
+                    allow = fminf(8.0f, 9.9657843f - __builtin_amdgcn_logf(max_halves(smax))) * inv_cs;
+                grow = mx > m_ref + allow;
                 m_new = grow ? mx : m_ref;
                 moff = (m_new == -__builtin_inff()) ? 0.0f : -m_new * cscale;
             }
