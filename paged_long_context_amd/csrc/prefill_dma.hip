@@ -338,15 +338,15 @@ void prefill_dma_kernel(PrefillParams p) {
     }
     int bcur = 0;                                    // buffer of subtile j
 
-    // one subtile j of the range (buffer bcur)
-    auto sub = [&](auto mtag, int j) __attribute__((always_inline)) {
+    // one subtile j of the range (buffer bcur): the softmax of S(j), in sc,
+    // and S(j + 1) into sn
+    auto sub = [&](auto mtag, int j, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(mtag)::value;
         constexpr int RM = 16 / NM, RE = 16 / NE;    // scores per max step, per exp step
         const int bn = (bcur + 1 == NBS) ? 0 : bcur + 1, bnn = (bn + 1 == NBS) ? 0 : bn + 1;
         const uint32_t kbn = sk0 + bn * CB;          // K codes of subtile j + 1
         const uint32_t vbc = sv0 + bcur * CB;        // V codes of subtile j
         const int k0 = 32 * (jb + j);                // its first key
-        f32x16 sn;
         float mloc = -__builtin_inff(), mx = 0.0f, m_new = 0.0f, moff = 0.0f, psum = 0.0f, smax = 0.0f;
         bool grow = false;
         f16x8 pp[2], kop[2];
@@ -428,7 +428,13 @@ void prefill_dma_kernel(PrefillParams p) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[dt][r] = scale_acc(acc[dt][r], alpha);
+                for (int r = 0; r < 16; ++r) {
+                    // head dim 128: every accumulator has a VGPR home (about
+                    // 186 registers in all), so S needs no copy out of AGPRs
+                    // before the softmax; 256: O stays in AGPRs
+                    if constexpr (DH == 256) acc[dt][r] = scale_acc(acc[dt][r], alpha);
+                    else acc[dt][r] *= alpha;
+                }
             asm volatile("s_nop 7" ::: "memory");
         }
         m_ref = m_new;
@@ -471,13 +477,27 @@ void prefill_dma_kernel(PrefillParams p) {
             if (i >= NQ - PFK) kraw[i - (NQ - PFK)] = kread(sk0 + bnn * CB, i - (NQ - PFK));   // subtile j + 2
             step_fence();
         }
-        sc = sn;
         bcur = bn;
     };
-    using U = std::false_type;
-    using M = std::true_type;
-    for (int j = 0; j < nfloc; ++j) sub(U{}, j);
-    for (int j = nfloc; j < nloc; ++j) sub(M{}, j);
+    // Head dim 128 takes two subtiles per iteration, the score tiles trading
+    // roles, so that no copy moves S(j + 1) into place (at 256 the pair
+    // raised the register count from 296 to 407)
+    f32x16 sb;
+    auto run = [&](auto mtag, int j0, int j1) __attribute__((always_inline)) {
+        int j = j0;
+        if constexpr (DH == 128) {
+            for (; j + 1 < j1; j += 2) {
+                sub(mtag, j, sc, sb);
+                sub(mtag, j + 1, sb, sc);
+            }
+        }
+        for (; j < j1; ++j) {
+            sub(mtag, j, sc, sb);
+            sc = sb;
+        }
+    };
+    run(std::false_type{}, 0, nfloc);
+    run(std::true_type{}, nfloc, nloc);
     // DMAs still in flight write this workgroup's LDS: let them land first
     wait_vm<0>();
 
