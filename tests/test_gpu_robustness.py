@@ -99,6 +99,54 @@ def test_int8_verify_with_fp16_extreme_values(plc, d, hq, hkv, n):
     print("int8 verify d%d n=%d: max|do|/max|V| %.2e" % (d, n, e), flush=True)
 
 
+def rising_scores(w, seed, bits_per_key=1.0 / 64):
+    """Overwrite Q and K in place so that every query row's score rises by
+    about bits_per_key (log2 units) per key position: each KV head gets a unit
+    direction u, its query rows are 8u and key t is beta * t * u.  A row's
+    running maximum then grows by about half a bit per 32-key subtile, so a
+    lazily kept reference maximum lags the true one by whatever slack the
+    kernel allows."""
+    s = w.spec
+    g = np.random.default_rng(seed)
+    G = s.num_q_heads // s.num_kv_heads
+    u = g.standard_normal((s.num_kv_heads, s.head_dim))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    amp = 8.0
+    beta = bits_per_key / (amp * sm_scale(s.head_dim) * np.log2(np.e))
+    for h in range(s.num_kv_heads):
+        w.q[:, h * G:(h + 1) * G, :] = (amp * u[h]).astype(np.float16)
+    for b in range(s.num_seqs):
+        a, e = int(w.cu_kv[b]), int(w.cu_kv[b + 1])
+        t = np.arange(e - a, dtype=np.float64)[:, None, None]
+        w.k[a:e] = (beta * t * u[None]).astype(np.float16)
+
+
+@pytest.mark.parametrize("call,d,hq,hkv,n,part", [
+    ("verify", 128, 8, 1, 16, 0), ("verify", 128, 8, 1, 16, 1024), ("verify", 256, 12, 2, 16, 0),
+    ("prefill", 256, 12, 2, 300, 0)])
+def test_int8_tiles_rising_maximum_with_fp16_extreme_values(plc, call, d, hq, hkv, n, part):
+    """The prefill tiles keep a lazy reference maximum.  INT8's P operand
+    carries 64 sigma_v, so with sigma_v near 65504 / 127 the slack must shrink
+    to about one bit or P overflows fp16; here every row's maximum keeps
+    rising through the keys, which is where a lagging reference would let P
+    grow.  16 drafts (and a 300-token chunk at head dim 256) run as tiles."""
+    q_lens = [n, n, min(n, 40)]
+    w = synthetic.generate(cases.spec([3000, 1500, 40], q_lens, hq=hq, hkv=hkv, d=d, seed=851 + d + n))
+    rising_scores(w, 852 + d)
+    vmax = big_values(w, 853)
+    cache, bt = device_cache(plc, w, "int8")
+    if call == "verify":
+        o, l = plc.attn_verify_paged(dev(w.q), cache, bt, dev(w.cu_q_lens), dev(w.context_lens), n, 3000,
+                                     part, sm_scale(d))
+    else:
+        o, l = plc.attn_prefill_paged(dev(w.q), cache, bt, dev(w.cu_q_lens), dev(w.context_lens), n, 3000,
+                                      sm_scale(d))
+    torch.cuda.synchronize()
+    ro, rl = cases.oracle_attention(w, cases.oracle_cache(w, "int8"), sm_scale(d))
+    e = assert_close_scaled(host(o), host(l), ro, rl, vmax, "int8 %s d%d rising max" % (call, d))
+    print("int8 %s d%d P=%d rising max: max|do|/max|V| %.2e" % (call, d, part, e), flush=True)
+
+
 @pytest.mark.parametrize("dtype", ["e4m3", "int8"])
 def test_workspace_reused_across_shapes(plc, dtype):
     """One workspace, never initialized (filled with NaN bytes here), serves
