@@ -258,9 +258,10 @@ int plc_attn_decode_append_noalloc(const void* q, const void* k_new, const void*
  *      counts are a prefill: PLC_ERR_INVALID_ARG); n_b above it is clamped.
  *  partition_tokens: as for plc_attn_decode_paged (0 = automatic).
  *  workspace: plc_verify_workspace_size bytes.
- * With an E4M3 or INT8 cache and more than 64 rows per (sequence, KV head)
- * (max_q_len x the group size; more than 32 at head_dim 256), the rows run
- * as 128-row tiles of the prefill kernel over key partitions (an explicit
+ * With more than 64 rows per (sequence, KV head) (max_q_len x the group
+ * size) of an E4M3 or INT8 cache, more than 32 at head_dim 256, or more than
+ * 32 of an FP16 cache at head_dim 128, the rows run as 128-row tiles of the
+ * prefill kernel over key partitions (an explicit
  * partition_tokens is rounded up to a multiple of 32; 0 sizes them for
  * about one workgroup per compute unit), merged as above; the results obey
  * the same bounds.

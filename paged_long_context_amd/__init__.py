@@ -394,8 +394,9 @@ def attn_verify_paged(q: torch.Tensor, cache: KVCache, block_tables: torch.Tenso
                       stream=None):
     """Verification decode: a few query tokens per sequence (the last n_b
     positions), causal among themselves, split-KV and merged in the same call
-    (with an 8-bit cache and many rows per KV head, as prefill tiles over key
-    partitions); q fp16 [T][Hq][D] -> (out fp32 [T][Hq][D], lse fp32 [T][Hq])."""
+    (with many rows per KV head, as prefill tiles over key partitions: 8-bit
+    caches at head dims 128 and 256, FP16 at 128); q fp16 [T][Hq][D] ->
+    (out fp32 [T][Hq][D], lse fp32 [T][Hq])."""
     return attn_window_paged(q, cache, block_tables, cu_q_lens, context_lens, max_q_len,
                              max_context_len, 0, partition_tokens, sm_scale, out, lse, workspace,
                              stream)

@@ -236,19 +236,28 @@ void mq_partitions(int32_t groups, int32_t num_kv_heads, int32_t max_q_len, int3
 
 // Calls with a few query tokens per sequence whose rows of one (sequence, KV
 // head) (drafted positions x heads) exceed a few 16-row groups run as the
-// 128-row tiles of the 8-bit prefill kernel over key partitions, merged
-// afterwards: a tile shares each converted K and V subtile among 128 rows
-// where a decode workgroup shares it among 16 or 32.  E4M3 and INT8 caches
-// without a window (FP16 caches and windows keep the decode kernel).  The
-// row counts above which tiles win, measured over 8 x 32K contexts (E4M3):
-// head dim 128 (G = 8): 64 rows 28.9 us by the decode kernel against 34.3 by
-// tiles, 80 rows 42.8 against 35.3, 128 rows 43.8 against 38.1; head dim 256
-// (G = 6): 24 rows 69 against 89, 48 rows 123 against 94, 96 rows 227
-// against 98.
+// 128-row tiles of the prefill DMA kernel over key partitions, merged
+// afterwards: a tile shares each K and V subtile among 128 rows where a
+// decode workgroup shares it among 16 or 32.  Calls without a window, 8-bit
+// caches at head dims 128 and 256, FP16 at 128 (windows, and FP16 at 256,
+// keep the decode kernel).  The row counts above which tiles win, measured
+// over 8 x 32K contexts:
+// - E4M3, head dim 128 (G = 8): 64 rows 28.9 us by the decode kernel against
+//   34.3 by tiles, 80 rows 42.8 against 35.3, 128 rows 43.8 against 38.1;
+// - E4M3, head dim 256 (G = 6): 24 rows 69 against 89, 48 rows 123 against
+//   94, 96 rows 227 against 98;
+// - FP16, head dim 128 (G = 8): 24 rows 34.6 against 38.8, 32 rows 34.9
+//   against 38.0, 48 rows 51.9 against 38.3, 64 rows 51.3 against 38.9, 128
+//   rows 87.7 against 42.7.
 constexpr int32_t kTileRows = 128;
 
-bool tile_eligible(int32_t head_dim, int32_t window, int32_t max_q_len, int32_t group) {
-    return window == 0 && (int64_t)max_q_len * group > (head_dim == kHeadDimWide ? 32 : 64);
+int64_t tile_row_threshold(int32_t dtype, int32_t head_dim) {
+    if (head_dim == kHeadDimWide) return dtype == PLC_KV_FP16 ? INT64_MAX : 32;
+    return dtype == PLC_KV_FP16 ? 32 : 64;
+}
+
+bool tile_eligible(int32_t dtype, int32_t head_dim, int32_t window, int32_t max_q_len, int32_t group) {
+    return window == 0 && (int64_t)max_q_len * group > tile_row_threshold(dtype, head_dim);
 }
 
 // Key partitions of the tile path: an explicit size rounded up to whole
@@ -502,8 +511,10 @@ size_t plc_window_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32
     const int32_t rg = plc::groups_per_workgroup(head_dim, true, ncg, P);
     size_t need = decode_partial_bytes(rows, (int64_t)num_seqs * num_kv_heads, (ncg + rg - 1) / rg, nparts,
                                        P, head_dim);
-    // the cache's dtype is not an argument: room for the tile path as well
-    if (tile_eligible(head_dim, window_tokens, max_q_len, num_q_heads / num_kv_heads)) {
+    // the cache's dtype is not an argument: room for the tile path of any dtype
+    const int32_t group = num_q_heads / num_kv_heads;
+    if (tile_eligible(PLC_KV_FP16, head_dim, window_tokens, max_q_len, group) ||
+        tile_eligible(PLC_KV_E4M3, head_dim, window_tokens, max_q_len, group)) {
         int32_t Pt = 0, npt = 0;
         tile_partitions(tile_units(num_seqs, num_q_heads, num_kv_heads, max_q_len), max_context_len,
                         partition_tokens, &Pt, &npt);
@@ -548,8 +559,7 @@ int plc_attn_window_paged(const void* q, int32_t num_q_heads, const plc_kv_cache
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
         return fail(PLC_ERR_INVALID_ARG, "sm_scale must be positive and finite");
     const size_t rows = (size_t)total_q_tokens * num_q_heads;
-    if (kv->dtype != PLC_KV_FP16 &&
-        tile_eligible(kv->head_dim, window_tokens, max_q_len, num_q_heads / kv->num_kv_heads)) {
+    if (tile_eligible(kv->dtype, kv->head_dim, window_tokens, max_q_len, num_q_heads / kv->num_kv_heads)) {
         int32_t Pt = 0, npt = 0;
         tile_partitions(tile_units(num_seqs, num_q_heads, kv->num_kv_heads, max_q_len), max_context_len,
                         partition_tokens, &Pt, &npt);

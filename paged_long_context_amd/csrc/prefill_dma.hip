@@ -1,7 +1,9 @@
-// Attention tiles of 128 query rows over 8-bit KV caches (E4M3, INT8) whose
-// codes reach LDS by DMA, at head dim 128 and 256, for gfx950: the chunked
-// causal prefill at head dim 256, and key partitions of the same tiles for
-// calls with up to 16 query tokens per sequence whose rows fill a tile.
+// Attention tiles of 128 query rows over paged KV caches whose rows reach LDS
+// by DMA, for gfx950: 8-bit codes (E4M3, INT8) at head dims 128 and 256, and
+// FP16 values at head dim 128 (rows of 256 bytes, like 256 codes).  They
+// serve the chunked causal prefill at head dim 256 (8-bit), and key
+// partitions of the same tiles for calls with up to 16 query tokens per
+// sequence whose rows fill a tile.
 //
 // A workgroup is 4 waves = 128 query rows of one (sequence, KV head),
 // position-major (row r = query token r / G, head r % G, so the G heads of a
@@ -15,14 +17,15 @@
 // 32 (two 16-token pages); subtiles wholly below the tile's first position
 // skip the causal mask (Layer 2 "Prefix / Causal-Tail Separation").
 //
-// The codes of each subtile reach LDS unconverted, by DMA (16 bytes per lane,
+// The rows of each subtile reach LDS unconverted, by DMA (16 bytes per lane,
 // one contiguous kilobyte per instruction, no registers involved), NBS
-// subtiles ahead of use; each wave converts the K and V operands it reads
-// (the pages keep the same goals with register prefetch on V100: Layer 1 and
-// "Software-Reconstructed Async").  V^T operands come from V stored as
-// [key][d] through the gfx950 transposing read (ds_read_b64_tr_b8: within
-// each 16 lanes, lane 8p + i receives byte i of the eight rows that lanes p,
-// p + 2, ..., p + 14 address).
+// subtiles ahead of use; each wave converts the 8-bit K and V operands it
+// reads, and FP16 values are operands as they stand (the pages keep the same
+// goals with register prefetch on V100: Layer 1 and "Software-Reconstructed
+// Async").  V^T operands come from V stored as [key][d] through the gfx950
+// transposing reads (ds_read_b64_tr_b8: within each 16 lanes, lane 8p + i
+// receives byte i of the eight rows that lanes p, p + 2, ..., p + 14
+// address; ds_read_b64_tr_b16 for FP16, below).
 //
 // Key partitions (Layer 2 "Split-KV3": partial states in fp32, merged after):
 // with partition_tokens > 0 the grid holds one workgroup per (row tile,
@@ -40,35 +43,40 @@ namespace {
 constexpr int BS = 16;
 constexpr int ROWS = 128;               // query rows per workgroup
 constexpr int NBS = 6;                  // 32-key code buffers in flight
-constexpr int PFK = 3;                  // K code pairs read this many pairs ahead
 constexpr int PFV = 5;                  // V operands read this many MFMAs ahead
 
 // all zeros: the DMA source of pages whose id is outside the pool (one
 // (page, head) slice at the widest head)
 __device__ __attribute__((aligned(16))) uint8_t g_zero_page[BS * 256];
 
-// Shapes of the key loop per head dim.
-template <int DH>
+// Shapes of the key loop per head dim DH and cache element bytes EB (1 for
+// the 8-bit codes; 2 for FP16, at head dim 128 only).
+template <int DH, int EB>
 struct Geo {
-    static_assert(DH == 128 || DH == 256, "head dim");
+    static_assert((DH == 128 || DH == 256) && (EB == 1 || (EB == 2 && DH == 128)), "head dim");
+    static constexpr int RB = DH * EB;      // bytes of one K (or V) row
     static constexpr int NQ = DH / 16;      // K MFMAs per subtile = PV MFMAs = steps per part
     static constexpr int NDT = DH / 32;     // O^T accumulator tiles
-    static constexpr int NKP = DH / 32;     // 32-code K pairs per row
-    static constexpr int NCH = DH / 16;     // 16-byte chunks per row
-    static constexpr int CB = 32 * DH;      // bytes of one subtile's K (or V) codes
-    static constexpr int NDK = DH / 128;    // K (and V) DMAs per wave per subtile
-    static constexpr int RPD = 1024 / DH;   // rows one DMA moves
+    static constexpr int KPR = 2 / EB;      // K operands per 16-byte read (a code pair, or one fp16 operand)
+    static constexpr int NKP = NQ / KPR;    // K reads per row
+    static constexpr int PFK = EB == 1 ? 3 : 4;   // K reads issued this many reads ahead
+    static constexpr int NCH = RB / 16;     // 16-byte chunks per row
+    static constexpr int CB = 32 * RB;      // bytes of one subtile's K (or V) rows
+    static constexpr int NDK = RB / 128;    // K (and V) DMAs per wave per subtile
+    static constexpr int RPD = 1024 / RB;   // rows one DMA moves
     static constexpr int NM = DH == 256 ? 4 : 2;   // part A steps of the row maximum
     static constexpr int NE = DH == 256 ? 8 : 4;   // part A steps of the exponentials
-    // chunk slot swizzles.  Chunk c (16 codes) of K row rho sits at slot
+    // chunk slot swizzles.  Chunk c (16 bytes) of K row rho sits at slot
     // c ^ kswz(rho), chunk c of V row (key) k at slot c ^ vswz(k).  A K operand
     // read (16 consecutive rows, one chunk) and a V transposing read (eight
-    // rows x two adjacent chunks per 32 lanes) then touch distinct banks:
-    // 256-byte rows all start on bank 0, so 16 distinct slots cover the 64
-    // banks; 128-byte rows alternate between banks 0 and 32, so the slot of
-    // rows of one parity must differ.
-    __device__ static int kswz(int rho) { return DH == 256 ? (rho & 15) : ((rho >> 1) & 7); }
+    // rows x two adjacent chunks per 32 lanes for 8-bit codes; four rows x
+    // four adjacent chunks for fp16) then touch distinct banks: 256-byte rows
+    // all start on bank 0, so 16 distinct slots cover the 64 banks; 128-byte
+    // rows alternate between banks 0 and 32, so the slot of rows of one
+    // parity must differ.
+    __device__ static int kswz(int rho) { return RB == 256 ? (rho & 15) : ((rho >> 1) & 7); }
     __device__ static int vswz(int k) {
+        if (EB == 2) return 4 * (k & 3);
         return DH == 256 ? (((k & 7) << 1) | ((k >> 3) & 1)) : (((k >> 1) & 3) << 1);
     }
 };
@@ -115,13 +123,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Subtile x is first read at the end of part B of x - 2, after the barrier
 // of x - 2, by which every wave has waited for its own DMAs of x.  Subtiles
 // are counted from the first of the workgroup's key range.
+// One wave per SIMD where the LDS holds one workgroup per CU (head dim 256,
+// and fp16 rows of 256 bytes); two at head dim 128 with 8-bit codes.
 template <int KV, int DH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DH == 256 ? 1 : 2, DH == 256 ? 1 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DH == 256 || KV == KV_FP16 ? 1 : 2,
+                                                                     DH == 256 || KV == KV_FP16 ? 1 : 2)))
 void prefill_dma_kernel(PrefillParams p) {
-    static_assert(KV != KV_FP16, "8-bit codes");
-    using Gm = Geo<DH>;
+    using Gm = Geo<DH, KV == KV_FP16 ? 2 : 1>;
     constexpr int NQ = Gm::NQ, NDT = Gm::NDT, NKP = Gm::NKP, NCH = Gm::NCH, CB = Gm::CB;
     constexpr int NDK = Gm::NDK, RPD = Gm::RPD, NM = Gm::NM, NE = Gm::NE;
+    constexpr int RB = Gm::RB, KPR = Gm::KPR, PFK = Gm::PFK;
+    // V operands in flight: 8 codes, or 8 fp16 values
+    using VR = std::conditional_t<KV == KV_FP16, u32x4, u32x2>;
     // DMA instructions per subtile per wave: codes (2 NDK), INT8 scales (1), page ids (1)
     constexpr int ND = 2 * NDK + 1 + (KV == KV_INT8 ? 1 : 0);
     // part A: INT8 scale reads, row maximum, its exchange, exponentials
@@ -207,14 +220,17 @@ void prefill_dma_kernel(PrefillParams p) {
     // clamp to the range's last page (prefetches past the range reread it)
     const int plast = min((kend - 1) / BS, 2 * je - 1) - 2 * jb;
 
-    // Q operands.  MFMA kc of a subtile takes half (kc & 1) of K code pair
-    // kc >> 1, whose lane (row, h32) holds d = 32(kc>>1) + 16 h32 + [0,16), so
-    // lane (row, h32) of qop[kc] holds d = 32(kc>>1) + 16 h32 + 8(kc&1) + [0,8).
+    // Q operands.  8-bit codes: MFMA kc of a subtile takes half (kc & 1) of K
+    // code pair kc >> 1, whose lane (row, h32) holds d = 32(kc>>1) + 16 h32 +
+    // [0,16), so lane (row, h32) of qop[kc] holds d = 32(kc>>1) + 16 h32 +
+    // 8(kc&1) + [0,8).  FP16: MFMA kc takes K read kc, whose lane (row, h32)
+    // holds d = 16 kc + 8 h32 + [0,8), and so does qop[kc].
     f16x8 qop[NQ];
     {
-        const f16* q = static_cast<const f16*>(p.q) + rowid * DH + 16 * h32;
+        const f16* q = static_cast<const f16*>(p.q) + rowid * DH + (KPR == 2 ? 16 : 8) * h32;
 #pragma unroll
-        for (int kc = 0; kc < NQ; ++kc) qop[kc] = *reinterpret_cast<const f16x8*>(q + 32 * (kc >> 1) + 8 * (kc & 1));
+        for (int kc = 0; kc < NQ; ++kc)
+            qop[kc] = *reinterpret_cast<const f16x8*>(q + (KPR == 2 ? 32 * (kc >> 1) + 8 * (kc & 1) : 16 * kc));
     }
     float cscale = p.qk_scale_log2;
     if constexpr (KV == KV_E4M3) cscale *= p.kv.k_scale[kvh];
@@ -241,10 +257,10 @@ void prefill_dma_kernel(PrefillParams p) {
     for (int h = 0; h < NDK; ++h) {
         const int row = 16 * h + RPD * wave + lane / NCH, slot = lane % NCH;
         const int kk = key_of_row(row) & 15;
-        kof[h] = (uint32_t)(kk * DH + 16 * (slot ^ Gm::kswz(row)));
-        vof[h] = (uint32_t)((row & 15) * DH + 16 * (slot ^ Gm::vswz(row)));
+        kof[h] = (uint32_t)(kk * RB + 16 * (slot ^ Gm::kswz(row)));
+        vof[h] = (uint32_t)((row & 15) * RB + 16 * (slot ^ Gm::vswz(row)));
     }
-    const int64_t head_off = (int64_t)kvh * BS * DH;
+    const int64_t head_off = (int64_t)kvh * BS * RB;
     // the zero page's address, loaded once and kept in scalar registers
     uint64_t zp = reinterpret_cast<uint64_t>(&g_zero_page[0]);
     asm volatile("" : "+s"(zp));
@@ -252,7 +268,7 @@ void prefill_dma_kernel(PrefillParams p) {
     // selected with masks (uniform arithmetic, no branch)
     auto page_base = [&](const void* cache, int pg) __attribute__((always_inline)) -> const uint8_t* {
         const uint64_t m = 0ull - (uint64_t)((uint32_t)pg < (uint32_t)p.kv.num_blocks);
-        const uint64_t a = reinterpret_cast<uint64_t>(cache) + (uint64_t)((int64_t)pg * Hkv * BS * DH + head_off);
+        const uint64_t a = reinterpret_cast<uint64_t>(cache) + (uint64_t)((int64_t)pg * Hkv * BS * RB + head_off);
         return reinterpret_cast<const uint8_t*>((a & m) | (zp & ~m));
     };
     // INT8 scales of subtile x: lane l < 32 reads key l's K scale, lane 32 + l
@@ -268,8 +284,8 @@ void prefill_dma_kernel(PrefillParams p) {
         for (int h = 0; h < NDK; ++h) {
             const int first = 16 * h + RPD * wave;   // wave-uniform
             const int pg = (first >> 4) ? pg1 : pg0;
-            dma16s(page_base(p.kv.k, pg), kof[h], lk + first * DH);
-            dma16s(page_base(p.kv.v, pg), vof[h], lv + first * DH);
+            dma16s(page_base(p.kv.k, pg), kof[h], lk + first * RB);
+            dma16s(page_base(p.kv.v, pg), vof[h], lv + first * RB);
         }
         if constexpr (KV == KV_INT8) {
             const int key = lane & 31;
@@ -296,26 +312,52 @@ void prefill_dma_kernel(PrefillParams p) {
     wait_vm<(NBS - 3) * ND>();
     __syncthreads();
 
-    // ---- operand reads.  K code pair q of buffer bi: lane (r32, h32) reads
-    // 16 codes of row r32, chunk 2q + h32, at (kb + ka) ^ 32q; V operand
-    // (dt, hf): the transposing read at ((vb + va) ^ 32dt) + 16 DH hf.
-    const uint32_t ka = (uint32_t)(r32 * DH + 16 * (h32 ^ Gm::kswz(r32)));
+    // ---- operand reads.  K read q of buffer bi: lane (r32, h32) reads the
+    // 16 bytes of row r32, chunk 2q + h32, at (kb + ka) ^ 32q.  V operand
+    // (dt, hf), 8-bit codes: the transposing read at ((vb + va) ^ 32dt) +
+    // 16 RB hf.  FP16: two 16-bit transposing reads (ds_read_b64_tr_b16:
+    // within each 16 lanes, lane 4p + i receives element i of the four rows
+    // that lanes p, p + 4, p + 8, p + 12 address, measured with a probe) at
+    // ((vb + va) ^ 64dt) + 16 RB hf and 4 rows further: lane (q, p) of a
+    // 16-lane group (q = (l & 15) >> 2, p = l & 3) addresses key 8 h32 + q,
+    // dimensions 16 gp + 4p + [0,4) of the tile, so lane l receives keys
+    // 8 h32 + [0,4) (then + [4,8)) of dimension l % 32.
+    const uint32_t ka = (uint32_t)(r32 * RB + 16 * (h32 ^ Gm::kswz(r32)));
     uint32_t va;
-    {
+    if constexpr (KV == KV_FP16) {
+        // chunk 4dt + 2gp + (p >> 1) of key k at slot c ^ 4(k & 3), k & 3 = q
+        const int q4 = (lane & 15) >> 2, p4 = lane & 3, gp = (lane >> 4) & 1;
+        va = (uint32_t)((8 * h32 + q4) * RB + 64 * q4 + 32 * gp + 8 * p4);
+    } else {
         const int key = 8 * h32 + ((lane & 15) >> 1), gp = (lane >> 4) & 1;
-        va = (uint32_t)(key * DH + 16 * (gp ^ Gm::vswz(key)) + 8 * (lane & 1));
+        va = (uint32_t)(key * RB + 16 * (gp ^ Gm::vswz(key)) + 8 * (lane & 1));
     }
     const uint32_t sk0 = lds_addr(&s_kv[0][0][0]), sv0 = lds_addr(&s_kv[1][0][0]);
     auto kread = [&](uint32_t kb, int q) __attribute__((always_inline)) {
         return *(__attribute__((address_space(3))) const u32x4*)(uintptr_t)((kb + ka) ^ (32u * q));
     };
-    auto vread = [&](uint32_t vb, int dt, int hf) __attribute__((always_inline)) {
-        typedef int v2i __attribute__((ext_vector_type(2)));
-        const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(uintptr_t)(((vb + va) ^ (32u * dt)) + 16u * DH * hf));
-        return u32x2{(uint32_t)r[0], (uint32_t)r[1]};
+    auto vread = [&](uint32_t vb, int dt, int hf) __attribute__((always_inline)) -> VR {
+        if constexpr (KV == KV_FP16) {
+            typedef short v4s __attribute__((ext_vector_type(4)));
+            const uint32_t a = ((vb + va) ^ (64u * dt)) + 16u * RB * hf;
+            const u32x2 r0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(uintptr_t)a));
+            const u32x2 r1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(uintptr_t)(a + 4u * RB)));
+            return u32x4{r0[0], r0[1], r1[0], r1[1]};
+        } else {
+            typedef int v2i __attribute__((ext_vector_type(2)));
+            const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i*)(uintptr_t)(((vb + va) ^ (32u * dt)) + 16u * RB * hf));
+            return u32x2{(uint32_t)r[0], (uint32_t)r[1]};
+        }
     };
 
+    // operand `half` of K read w (fp16: the read itself)
+    auto kop_of = [&](const u32x4& w, int half) __attribute__((always_inline)) -> f16x8 {
+        if constexpr (KPR == 1) return __builtin_bit_cast(f16x8, w);
+        else return half ? codes8_to_f16x8<KV>(w[2], w[3]) : codes8_to_f16x8<KV>(w[0], w[1]);
+    };
     // ---- S of subtile 0
     f32x16 sc;
     {
@@ -323,14 +365,10 @@ void prefill_dma_kernel(PrefillParams p) {
 #pragma unroll
         for (int q = 0; q < NKP; ++q) raw[q] = kread(sk0, q);
 #pragma unroll
-        for (int kc = 0; kc < NQ; ++kc) {
-            const u32x4& w = raw[kc >> 1];
-            const f16x8 kop = (kc & 1) ? codes8_to_f16x8<KV>(w[2], w[3]) : codes8_to_f16x8<KV>(w[0], w[1]);
-            sc = mfma32(kop, qop[kc], kc ? sc : f32x16{});
-        }
+        for (int kc = 0; kc < NQ; ++kc) sc = mfma32(kop_of(raw[kc / KPR], kc & 1), qop[kc], kc ? sc : f32x16{});
     }
-    u32x4 kraw[PFK];                                 // K code pairs in flight (subtile j + 1)
-    u32x2 vraw[PFV];                                 // V operands in flight (subtile j)
+    u32x4 kraw[PFK];                                 // K reads in flight (subtile j + 1)
+    VR vraw[PFV];                                    // V operands in flight (subtile j)
     {
         const uint32_t kb1 = sk0 + CB;
 #pragma unroll
@@ -356,12 +394,18 @@ void prefill_dma_kernel(PrefillParams p) {
         // ---------------- part A
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
-            if ((i & 1) == 0) {
-                // pair i/2 arrived PFK pairs ago: both its operands, then the read PFK pairs ahead
-                const u32x4 w = kraw[(i >> 1) % PFK];
-                kop[0] = codes8_to_f16x8<KV>(w[0], w[1]);
-                kop[1] = codes8_to_f16x8<KV>(w[2], w[3]);
-                if ((i >> 1) + PFK < NKP) kraw[(i >> 1) % PFK] = kread(kbn, (i >> 1) + PFK);
+            if constexpr (KPR == 2) {
+                if ((i & 1) == 0) {
+                    // pair i/2 arrived PFK pairs ago: both its operands, then the read PFK pairs ahead
+                    const u32x4 w = kraw[(i >> 1) % PFK];
+                    kop[0] = kop_of(w, 0);
+                    kop[1] = kop_of(w, 1);
+                    if ((i >> 1) + PFK < NKP) kraw[(i >> 1) % PFK] = kread(kbn, (i >> 1) + PFK);
+                }
+            } else {
+                // read i arrived PFK reads ago: its operand, then the read PFK ahead
+                kop[i & 1] = kop_of(kraw[i % PFK], 0);
+                if (i + PFK < NKP) kraw[i % PFK] = kread(kbn, i + PFK);
             }
             sn = mfma32(kop[i & 1], qop[i], i ? sn : f32x16{});
             if (i >= NQ - PFV) vraw[i - (NQ - PFV)] = vread(vbc, (i - (NQ - PFV)) % NDT, (i - (NQ - PFV)) / NDT);
@@ -446,13 +490,22 @@ void prefill_dma_kernel(PrefillParams p) {
         // ---------------- part B
         // masked subtiles zero the V codes of keys past the visible end (the
         // cache holds garbage there, and P = 0 times a NaN code is NaN)
-        uint32_t vm[2][2];
+        // (a lane's operand of key half hf holds keys k0 + 16 hf + 8 h32 + [0,8)
+        // in order: 4 per dword of codes, 2 per dword of fp16 values)
+        constexpr int VW = sizeof(VR) / 4;           // dwords per V operand
+        uint32_t vm[2][VW];
         if constexpr (MASKED) {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int cnt = min(max(kend - (k0 + 16 * hf + 8 * h32), 0), 8);
-                vm[hf][0] = cnt >= 4 ? 0xFFFFFFFFu : (1u << (8 * cnt)) - 1u;
-                vm[hf][1] = cnt >= 8 ? 0xFFFFFFFFu : (cnt <= 4 ? 0u : (1u << (8 * (cnt - 4))) - 1u);
+                if constexpr (KV == KV_FP16) {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        vm[hf][x] = cnt >= 2 * x + 2 ? 0xFFFFFFFFu : (cnt == 2 * x + 1 ? 0x0000FFFFu : 0u);
+                } else {
+                    vm[hf][0] = cnt >= 4 ? 0xFFFFFFFFu : (1u << (8 * cnt)) - 1u;
+                    vm[hf][1] = cnt >= 8 ? 0xFFFFFFFFu : (cnt <= 4 ? 0u : (1u << (8 * (cnt - 4))) - 1u);
+                }
             }
         }
         f16x8 vop;
@@ -465,12 +518,13 @@ void prefill_dma_kernel(PrefillParams p) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             {
-                u32x2 w = vraw[i % PFV];
+                VR w = vraw[i % PFV];
                 if constexpr (MASKED) {
-                    w[0] &= vm[i / NDT][0];
-                    w[1] &= vm[i / NDT][1];
+#pragma unroll
+                    for (int x = 0; x < VW; ++x) w[x] &= vm[i / NDT][x];
                 }
-                vop = codes8_to_f16x8<KV>(w[0], w[1]);
+                if constexpr (KV == KV_FP16) vop = __builtin_bit_cast(f16x8, w);
+                else vop = codes8_to_f16x8<KV>(w[0], w[1]);
             }
             if (i + PFV < NQ) vraw[i % PFV] = vread(vbc, (i + PFV) % NDT, (i + PFV) / NDT);
             acc[i % NDT] = mfma32(vop, pp[i / NDT], acc[i % NDT]);
@@ -551,6 +605,10 @@ hipError_t launch_dh(const PrefillParams& p, hipStream_t s) {
     if (grid.x == 0) return hipSuccess;
     const dim3 block(256);
     switch (p.kv.dtype) {
+    case KV_FP16:
+        if constexpr (DH != 128) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((prefill_dma_kernel<KV_FP16, DH>), grid, block, 0, s, p);
+        break;
     case KV_E4M3: hipLaunchKernelGGL((prefill_dma_kernel<KV_E4M3, DH>), grid, block, 0, s, p); break;
     case KV_INT8: hipLaunchKernelGGL((prefill_dma_kernel<KV_INT8, DH>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;

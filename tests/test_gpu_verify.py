@@ -130,7 +130,7 @@ def test_verify_full_decode_shape_sampled(plc):
     assert_close(o, l, ro, rl, rows=rows, what="verify 8x32768 n=4")
 
 
-@pytest.mark.parametrize("dtype", ["e4m3", "int8"])
+@pytest.mark.parametrize("dtype", ["fp16", "e4m3", "int8"])
 def test_verify_tiles_edges(plc, dtype):
     # 16 drafts x 8 heads = 128 rows per (sequence, KV head): the 128-row
     # tiles over key partitions, then the merge.  The first sequence is given
