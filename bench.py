@@ -812,19 +812,20 @@ def bench_decode_config(plc, synthetic, specs, name, dtypes, cpu, w=None):
     return out
 
 
-def bench_verify(plc, synthetic, specs, widths=(4, 16), spec_name="verify"):
-    """Verification decode at the decode batch's shape (8 x 32768, E4M3,
-    automatic partitions), 8 rotated cache copies, for a few draft widths;
-    spec_name "d256" takes the head dim 256 batch (12 q / 2 kv) instead."""
+def bench_verify(plc, synthetic, specs, widths=(4, 16), spec_name="verify", dtype="e4m3"):
+    """Verification decode at the decode batch's shape (8 x 32768, E4M3 unless
+    dtype says otherwise, automatic partitions), 8 rotated cache copies, for a
+    few draft widths; spec_name "d256" takes the head dim 256 batch (12 q / 2
+    kv) instead."""
     import dataclasses
     res = {}
     for n in widths:
         sp = dataclasses.replace(specs[spec_name], q_lens=[n] * len(specs[spec_name].context_lens))
-        tag = "verify" if spec_name == "verify" else spec_name + " verify"
+        tag = ("verify" if spec_name == "verify" else spec_name + " verify") + ("" if dtype == "e4m3" else " " + dtype)
         log("generating %s n=%d" % (tag, n))
         w = synthetic.generate(sp)
         s = w.spec
-        caches, bt = build_cache(plc, w, "e4m3", 8)
+        caches, bt = build_cache(plc, w, dtype, 8)
         kn, vn = w.new_kv()
         kn, vn = to_dev(kn), to_dev(vn)
         cu, start, ctx = to_dev(w.cu_q_lens), to_dev(w.start_pos), to_dev(w.context_lens)
@@ -848,7 +849,7 @@ def bench_verify(plc, synthetic, specs, widths=(4, 16), spec_name="verify"):
             f(i)
         st, _ = timed(f, 30e-6, smi=False)
         ev = st["median_us"] * 1e-6
-        vb = verify_bytes(w, "e4m3")
+        vb = verify_bytes(w, dtype)
         L = w.context_lens.astype(np.int64)
         visible = int(sum(n * (int(l) - n) + n * (n + 1) // 2 for l in L))
         fl = 4 * s.head_dim * s.num_q_heads * visible
@@ -862,7 +863,8 @@ def bench_verify(plc, synthetic, specs, widths=(4, 16), spec_name="verify"):
             % (tag, n, ev * 1e6, vb / ev / 1e9, 100 * vb / ev / 1e9 / HBM_PEAK_GBS, fl / ev / 1e12))
         del caches, ws, out, lse, q
         torch.cuda.empty_cache()
-    res["workload"] = specs[spec_name].description + "; widths as listed"
+    res["workload"] = specs[spec_name].description + "; widths as listed" + \
+        ("" if dtype == "e4m3" else "; %s cache" % dtype.upper())
     return res
 
 
@@ -1040,6 +1042,8 @@ def main():
                 res["verify_e4m3"] = bench_verify(plc, synthetic, specs)
             elif name == "verify_d256":
                 res["verify_d256_e4m3"] = bench_verify(plc, synthetic, specs, widths=(16,), spec_name="d256")
+            elif name == "verify_fp16":
+                res["verify_fp16"] = bench_verify(plc, synthetic, specs, widths=(16,), dtype="fp16")
             elif name == "window":
                 res["draft_window_e4m3"] = bench_window(plc, synthetic, specs)
             elif name == "d256":
@@ -1072,6 +1076,7 @@ def main():
         extra.update(bench_decode_config(plc, synthetic, specs, "c5", ["fp16", "e4m3", "int8"], cpu))
         extra["verify_e4m3"] = bench_verify(plc, synthetic, specs)
         extra["verify_d256_e4m3"] = bench_verify(plc, synthetic, specs, widths=(16,), spec_name="d256")
+        extra["verify_fp16"] = bench_verify(plc, synthetic, specs, widths=(16,), dtype="fp16")
         extra["draft_window_e4m3"] = bench_window(plc, synthetic, specs)
         extra["d256_decode"] = bench_d256(plc, synthetic, specs)
         extra["d256_prefill"] = bench_d256_prefill(plc, synthetic, specs)
