@@ -94,28 +94,32 @@ def test_verify_causal_edge_keys(plc):
         assert_close(o, l, ro, rl, what="causal edge %s" % dtype)
 
 
-def test_verify_overflowing_logits(plc):
-    w = synthetic.generate(cases.spec([3000, 40], [4, 4], hq=8, hkv=1, seed=414, q_scale=900.0,
+@pytest.mark.parametrize("n", [4, 16])
+def test_verify_overflowing_logits(plc, n):
+    # 4 drafts x 8 heads: the decode kernel; 16: the tiles (every dtype)
+    w = synthetic.generate(cases.spec([3000, 40], [n, n], hq=8, hkv=1, seed=414, q_scale=900.0,
                                       v_dist="uniform"))
     for dtype in ["fp16", "e4m3", "int8"]:
         o, l = run_verify(plc, w, dtype, 1024)
         ro, rl = oracle_verify(w, dtype)
         assert np.abs(rl).max() > 1000
-        assert_close(o, l, ro, rl, what="verify overflow %s" % dtype)
+        assert_close(o, l, ro, rl, what="verify overflow %s n=%d" % (dtype, n))
 
 
-def test_verify_is_deterministic_and_placement_independent(plc):
-    w = synthetic.generate(cases.spec([5000, 1234], [4, 9], hq=8, hkv=1, seed=415))
-    cache, bt = device_cache(plc, w, "e4m3")
-    o1, l1 = run_verify(plc, w, "e4m3", 1024, cache, bt)
-    o2, l2 = run_verify(plc, w, "e4m3", 1024, cache, bt)
+@pytest.mark.parametrize("dtype,ql", [("e4m3", [4, 9]), ("fp16", [16, 11])])
+def test_verify_is_deterministic_and_placement_independent(plc, dtype, ql):
+    w = synthetic.generate(cases.spec([5000, 1234], ql, hq=8, hkv=1, seed=415))
+    cache, bt = device_cache(plc, w, dtype)
+    n = max(ql)
+    o1, l1 = run_verify(plc, w, dtype, 1024, cache, bt)
+    o2, l2 = run_verify(plc, w, dtype, 1024, cache, bt)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
     perm = np.random.default_rng(2).permutation(w.num_blocks).astype(np.int32)
     bt2 = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
     w2 = synthetic.Workload(**{**w.__dict__, "block_tables": bt2})
-    cache2, bt2d = device_cache(plc, w2, "e4m3")
-    o3, l3 = run_verify(plc, w2, "e4m3", 1024, cache2, bt2d)
-    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+    cache2, bt2d = device_cache(plc, w2, dtype)
+    o3, l3 = run_verify(plc, w2, dtype, 1024, cache2, bt2d)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3), "n=%d" % n
 
 
 def test_verify_full_decode_shape_sampled(plc):
