@@ -163,19 +163,20 @@ def test_verify_tiles_two_row_tiles_per_head(plc):
     # G = 16: 16 drafts x 16 heads = 256 rows per KV head, two tiles each,
     # two KV heads; mixed draft counts leave the second tile part-filled
     w = synthetic.generate(cases.spec([3000, 129, 2100], [16, 12, 5], hq=32, hkv=2, seed=418))
-    for dtype in ["e4m3", "int8"]:
+    for dtype in ["fp16", "e4m3", "int8"]:
         o, l = run_verify(plc, w, dtype, 0, max_q_len=16)
         ro, rl = oracle_verify(w, dtype)
         assert_close(o, l, ro, rl, what="verify G=16 tiles %s" % dtype)
 
 
-def test_verify16_full_shape_sampled(plc):
-    # the bench's 16-draft call at full size: 8 x 32768 context, 8 q / 1 kv,
+@pytest.mark.parametrize("dtype", ["e4m3", "fp16"])
+def test_verify16_full_shape_sampled(plc, dtype):
+    # the bench's 16-draft calls at full size: 8 x 32768 context, 8 q / 1 kv,
     # automatic partitions (128-row tiles over 32 partitions of 1,024 keys);
     # the oracle checks a seeded sample of rows spread over every sequence
     ctx = [32768] * 8
     w = synthetic.generate(cases.spec(ctx, [16] * 8, hq=8, hkv=1, seed=419))
     rows = np.sort(np.random.default_rng(419).choice(128 * 8, 48, replace=False))
-    o, l = run_verify(plc, w, "e4m3", 0)
-    ro, rl = oracle_verify(w, "e4m3", rows=rows)
-    assert_close(o, l, ro, rl, rows=rows, what="verify 8x32768 n=16")
+    o, l = run_verify(plc, w, dtype, 0)
+    ro, rl = oracle_verify(w, dtype, rows=rows)
+    assert_close(o, l, ro, rl, rows=rows, what="verify 8x32768 n=16 %s" % dtype)
